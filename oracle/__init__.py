@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for exact attention forward -- test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP path.
+"""
+from .attention import (  # noqa: F401
+    allowed_key_count,
+    allowed_mask,
+    attention_fp64,
+    attention_full_fp64,
+    attention_rows_fp64,
+    decode_bf16_bits,
+    effective_kv_len,
+    to_fp64,
+)

@@ -1,0 +1,356 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The pages print no worked numeric example, so every pin is one of: brute force
+on tiny inputs (a pure-Python loop written independently of the oracle, without
+the max shift and without numpy), a closed form, an invariant of the definition,
+or a library routine (scipy's softmax).  Each is chosen so that a plausible
+mistake in the oracle (a dropped scale, a strict causal compare, a transposed
+operand, padding ignored, missing normalisation, a wrong bf16 widening) fails
+at least one of them; test_mutants_are_caught plants such mistakes on the CPU
+and checks that they are caught.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oa
+
+
+# --------------------------------------------------------------------------
+# brute force: the operator graph (scores, mask, softmax, weighted sum) with
+# Python floats, math.exp and math.fsum, one query row at a time
+# --------------------------------------------------------------------------
+def brute_force(q, k, v, scale, causal, kv_len):
+    B, H, N, d = q.shape
+    out = np.zeros((B, H, N, d))
+    s = float(np.float32(scale))
+    for b in range(B):
+        L = N if kv_len is None else max(0, min(int(kv_len[b]), N))
+        for h in range(H):
+            for i in range(N):
+                keys = [j for j in range(N) if j < L and (not causal or j <= i)]
+                if not keys:
+                    continue
+                w = {}
+                for j in keys:
+                    dot = math.fsum(float(q[b, h, i, t]) * float(k[b, h, j, t]) for t in range(d))
+                    w[j] = math.exp(s * dot)
+                Z = math.fsum(w.values())
+                for t in range(d):
+                    out[b, h, i, t] = math.fsum(w[j] * float(v[b, h, j, t]) for j in keys) / Z
+    return out
+
+
+def _rand(shape, seed, sd=0.7):
+    return np.random.default_rng(seed).normal(0.0, sd, size=shape)
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("d", [1, 2, 4, 8])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("padded", [False, True])
+def test_brute_force_tiny(N, d, causal, padded):
+    seed = 100 * N + 10 * d + 2 * causal + padded
+    B, H = 2, 2
+    q, k, v = (_rand((B, H, N, d), seed + t) for t in range(3))
+    kv_len = None
+    if padded:
+        kv_len = np.random.default_rng(seed + 7).integers(0, N + 1, size=B)
+    scale = 1.0 / math.sqrt(d)
+    got = oracle.attention_fp64(q, k, v, scale, causal, kv_len, kind="f64")
+    ref = brute_force(q, k, v, scale, causal, kv_len)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_brute_force_bf16_bits():
+    """bf16 path: bit patterns from torch's round-to-nearest-even conversion."""
+    torch = pytest.importorskip("torch")
+    g = torch.Generator().manual_seed(5)
+    B, H, N, d = 1, 2, 7, 4
+    t = [torch.randn(B, H, N, d, generator=g).to(torch.bfloat16) for _ in range(3)]
+    bits = [x.view(torch.int16).numpy().view(np.uint16) for x in t]
+    vals = [x.to(torch.float64).numpy() for x in t]
+    kv = np.array([5])
+    got = oracle.attention_fp64(*bits, 0.5, True, kv, kind="bf16")
+    ref = brute_force(*vals, 0.5, True, kv)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# bf16 widening
+# --------------------------------------------------------------------------
+def test_bf16_decoder_known_patterns():
+    bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4000, 0xC040, 0x3F00, 0x7F80, 0xFF80,
+                     0x0001, 0x7F7F, 0x3E80], dtype=np.uint16)
+    want = [0.0, -0.0, 1.0, -1.0, 2.0, -3.0, 0.5, np.inf, -np.inf,
+            2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127, 0.25]
+    got = oa.decode_bf16_bits(bits)
+    for g_, w_ in zip(got, want):
+        assert g_ == w_ and math.copysign(1, g_) == math.copysign(1, w_)
+    assert np.isnan(oracle.decode_bf16_bits(np.array([0x7FC0], dtype=np.uint16))[0])
+
+
+def test_bf16_decoder_matches_torch():
+    torch = pytest.importorskip("torch")
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    tb = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    ours = oracle.decode_bf16_bits(allbits)
+    same = (ours == tb) | (np.isnan(ours) & np.isnan(tb))
+    assert same.all()
+
+
+def test_bf16_decoder_rejects_other_dtypes():
+    with pytest.raises(TypeError):
+        oracle.decode_bf16_bits(np.zeros(3, dtype=np.int32))
+
+
+# --------------------------------------------------------------------------
+# invariants and closed forms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows(causal):
+    B, H, N, d = 2, 3, 33, 8
+    q, k, v = (_rand((B, H, N, d), 11 + t, 1.5) for t in range(3))
+    kv = np.array([20, 33])
+    O, P, lse = oracle.attention_full_fp64(q, k, v, 0.35, causal, kv)
+    assert (P >= 0).all()
+    for b in range(B):
+        L = kv[b]
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        allowed = np.broadcast_to((j < L) & ((j <= i) if causal else True), (N, N))
+        assert (P[b][:, ~allowed] == 0).all()   # masked entries are exactly zero
+        np.testing.assert_allclose(P[b].sum(-1), 1.0, rtol=0, atol=1e-12)
+        # lse is log sum exp of the allowed scaled scores
+        S = float(np.float32(0.35)) * np.einsum("hid,hjd->hij", q[b], k[b])
+        S = np.where(allowed, S, -np.inf)
+        ref = np.log(np.exp(S).sum(-1))
+        np.testing.assert_allclose(lse[b], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values_give_that_constant(causal):
+    B, H, N, d = 1, 2, 50, 16
+    q, k = _rand((B, H, N, d), 1, 2.0), _rand((B, H, N, d), 2, 2.0)
+    c = _rand((d,), 3)
+    v = np.broadcast_to(c, (B, H, N, d)).copy()
+    O = oracle.attention_fp64(q, k, v, 0.25, causal, np.array([37]), kind="f64")
+    np.testing.assert_allclose(O, np.broadcast_to(c, O.shape), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_uniform_mean(causal):
+    B, H, N, d = 2, 1, 40, 8
+    q, k, v = (_rand((B, H, N, d), 20 + t) for t in range(3))
+    kv = np.array([40, 13])
+    O = oracle.attention_fp64(q, k, v, 0.0, causal, kv, kind="f64")
+    for b in range(B):
+        L = kv[b]
+        for i in range(N):
+            n = min(i + 1, L) if causal else L
+            want = v[b, 0, :n].mean(0)
+            np.testing.assert_allclose(O[b, 0, i], want, rtol=0, atol=1e-12)
+
+
+def test_zero_scale_causal_prefix_mean_cumsum():
+    N, d = 300, 4
+    v = _rand((1, 1, N, d), 30)
+    q = k = _rand((1, 1, N, d), 31)
+    O = oracle.attention_fp64(q, k, v, 0.0, True, None, kind="f64")
+    want = np.cumsum(v[0, 0], axis=0) / np.arange(1, N + 1)[:, None]
+    np.testing.assert_allclose(O[0, 0], want, rtol=0, atol=1e-12)
+
+
+def test_causal_first_row_and_single_key():
+    B, H, N, d = 1, 2, 9, 8
+    q, k, v = (_rand((B, H, N, d), 40 + t, 3.0) for t in range(3))
+    O = oracle.attention_fp64(q, k, v, 0.9, True, None, kind="f64")
+    np.testing.assert_array_equal(O[:, :, 0], v[:, :, 0])         # row 0 sees key 0 only
+    O1 = oracle.attention_fp64(q[:, :, :1], k[:, :, :1], v[:, :, :1], 0.9, False, None, kind="f64")
+    np.testing.assert_array_equal(O1, v[:, :, :1])                 # N = 1: O = V
+    O2 = oracle.attention_fp64(q, k, v, 0.9, False, np.array([1]), kind="f64")
+    np.testing.assert_array_equal(O2, np.broadcast_to(v[:, :, :1], O2.shape))  # kv_len = 1
+
+
+def test_fully_masked_rows_are_zero():
+    q, k, v = (_rand((2, 1, 6, 4), 50 + t) for t in range(3))
+    O = oracle.attention_fp64(q, k, v, 0.5, False, np.array([0, 6]), kind="f64")
+    assert (O[0] == 0).all() and np.isfinite(O).all()
+    O = oracle.attention_fp64(q, k, v, 0.5, True, np.array([0, -3]), kind="f64")  # clamped to 0
+    assert (O == 0).all()
+
+
+def test_kv_len_clamped_above():
+    q, k, v = (_rand((1, 1, 6, 4), 55 + t) for t in range(3))
+    a = oracle.attention_fp64(q, k, v, 0.5, False, np.array([600]), kind="f64")
+    b = oracle.attention_fp64(q, k, v, 0.5, False, None, kind="f64")
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_keys_contribute_nothing(causal):
+    B, H, N, d = 1, 2, 64, 16
+    q, k, v = (_rand((B, H, N, d), 60 + t) for t in range(3))
+    L = 41
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, L:] = _rand((B, H, N - L, d), 70, 50.0)
+    v2[:, :, L:] = _rand((B, H, N - L, d), 71, 50.0)
+    a = oracle.attention_fp64(q, k, v, 0.3, causal, np.array([L]), kind="f64")
+    b = oracle.attention_fp64(q, k2, v2, 0.3, causal, np.array([L]), kind="f64")
+    np.testing.assert_array_equal(a, b)
+    if causal:
+        # the future of row i never matters: perturbing keys > i leaves row i unchanged
+        i = 10
+        k3, v3 = k.copy(), v.copy()
+        k3[:, :, i + 1:] += 5.0
+        v3[:, :, i + 1:] -= 7.0
+        c = oracle.attention_fp64(q, k3, v3, 0.3, True, None, kind="f64")
+        a2 = oracle.attention_fp64(q, k, v, 0.3, True, None, kind="f64")
+        np.testing.assert_array_equal(a2[:, :, : i + 1], c[:, :, : i + 1])
+
+
+def test_ramp_closed_form():
+    """Q_i = u, K_j = t_j u with increasing t_j: the row maximum grows with every
+    key, and O_i[0] = sum_j j w_j / sum_j w_j with w_j = exp(s t_j |u|^2)."""
+    N, d = 200, 8
+    u = _rand((d,), 80)
+    u /= np.linalg.norm(u)
+    t = np.linspace(-3.0, 9.0, N)
+    q = np.broadcast_to(u, (1, 1, N, d)).copy()
+    k = (t[:, None] * u[None, :])[None, None]
+    v = np.zeros((1, 1, N, d))
+    v[0, 0, :, 0] = np.arange(N)
+    v[0, 0, :, 1] = 1.0
+    s = 1.75
+    O = oracle.attention_fp64(q, k, v, s, True, None, kind="f64")
+    s64 = float(np.float32(s))
+    for i in (0, 1, 57, 128, N - 1):
+        w = np.exp(s64 * t[: i + 1] - s64 * t[i])
+        want = (np.arange(i + 1) * w).sum() / w.sum()
+        assert abs(O[0, 0, i, 0] - want) <= 1e-10 * max(1.0, abs(want))
+        assert abs(O[0, 0, i, 1] - 1.0) <= 1e-12
+
+
+def test_permutation_and_shift_invariance():
+    B, H, N, d = 1, 1, 48, 8
+    q, k, v = (_rand((B, H, N, d), 90 + t) for t in range(3))
+    base = oracle.attention_fp64(q, k, v, 0.4, False, None, kind="f64")
+    perm = np.random.default_rng(91).permutation(N)
+    # jointly permuting keys and values leaves every row unchanged
+    pk = oracle.attention_fp64(q, k[:, :, perm], v[:, :, perm], 0.4, False, None, kind="f64")
+    np.testing.assert_allclose(pk, base, rtol=0, atol=1e-12)
+    # permuting queries permutes output rows
+    pq = oracle.attention_fp64(q[:, :, perm], k, v, 0.4, False, None, kind="f64")
+    np.testing.assert_allclose(pq, base[:, :, perm], rtol=0, atol=1e-12)
+    # adding one vector to every key adds a per-row constant to the scores
+    w = _rand((d,), 92)
+    sh = oracle.attention_fp64(q, k + w, v, 0.4, False, None, kind="f64")
+    np.testing.assert_allclose(sh, base, rtol=0, atol=1e-12)
+
+
+def test_matches_scipy_softmax():
+    special = pytest.importorskip("scipy.special")
+    B, H, N, d = 1, 2, 257, 32
+    q, k, v = (_rand((B, H, N, d), 95 + t, 1.2) for t in range(3))
+    s = 1 / math.sqrt(d)
+    O = oracle.attention_fp64(q, k, v, s, True, None, kind="f64")
+    s64 = float(np.float32(s))
+    for h in range(H):
+        S = s64 * q[0, h] @ k[0, h].T
+        S[np.triu_indices(N, 1)] = -np.inf
+        want = special.softmax(S, axis=-1) @ v[0, h]
+        np.testing.assert_allclose(O[0, h], want, rtol=0, atol=1e-12)
+
+
+def test_scale_is_the_fp32_value():
+    """The oracle uses fp32(scale) widened, not the fp64 number passed in."""
+    q, k, v = (_rand((1, 1, 5, 3), 96 + t, 4.0) for t in range(3))
+    s = 1 / math.sqrt(128)
+    a = oracle.attention_fp64(q, k, v, s, False, None, kind="f64")
+    b = oracle.attention_fp64(q, k, v, float(np.float32(s)), False, None, kind="f64")
+    np.testing.assert_array_equal(a, b)
+
+
+def test_row_selection_matches_full_output():
+    B, H, N, d = 2, 3, 70, 8
+    q, k, v = (_rand((B, H, N, d), 100 + t) for t in range(3))
+    kv = np.array([70, 31])
+    full = oracle.attention_fp64(q, k, v, 0.3, True, kv, kind="f64")
+    rows = np.random.default_rng(3).choice(B * H * N, 77, replace=False)
+    part = oracle.attention_fp64(q, k, v, 0.3, True, kv, kind="f64", rows=rows, chunk=16)
+    np.testing.assert_allclose(part, full.reshape(-1, d)[rows], rtol=0, atol=1e-13)
+
+
+def test_input_validation():
+    x = np.zeros((1, 1, 4, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_fp64(x, x[:, :, :3], x, 1.0, kind="f64")
+    with pytest.raises(ValueError):
+        oracle.attention_fp64(x, x, x, 1.0, kind="f64", kv_len=np.array([1, 2]))
+    with pytest.raises(ValueError):
+        oracle.attention_fp64(x, x, x, 1.0, kind="f64", rows=np.array([4]))
+    with pytest.raises(TypeError):
+        oracle.attention_fp64(x, x, x, 1.0, kind="f32")
+
+
+# --------------------------------------------------------------------------
+# planted mistakes (on the CPU, in the oracle) must be caught by the pins
+# --------------------------------------------------------------------------
+def _pins_pass():
+    try:
+        test_brute_force_tiny(5, 4, True, True)
+        test_brute_force_tiny(8, 2, False, True)
+        test_probability_rows(True)
+        test_masked_keys_contribute_nothing(False)
+        test_bf16_decoder_known_patterns()
+        test_brute_force_bf16_bits()
+        test_causal_first_row_and_single_key()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_mutants_are_caught(monkeypatch):
+    assert _pins_pass()
+    real_mask = oa.allowed_mask
+    real_soft = oa._softmax_rows
+    real_dec = oa.decode_bf16_bits
+    mutants = {
+        "strict_causal": lambda rows, n, L, c: real_mask(rows, n, L, c) & (
+            (np.arange(n)[None, :] < np.asarray(rows)[:, None]) if c else True),
+        "padding_ignored": lambda rows, n, L, c: real_mask(rows, n, n, c),
+        "off_by_one_padding": lambda rows, n, L, c: real_mask(rows, n, L + 1, c),
+    }
+    for name, fn in mutants.items():
+        monkeypatch.setattr(oa, "allowed_mask", fn)
+        assert not _pins_pass(), name
+        monkeypatch.setattr(oa, "allowed_mask", real_mask)
+
+    def unnormalised(S, ok):
+        P, lse = real_soft(S, ok)
+        return P * 1.01, lse
+    monkeypatch.setattr(oa, "_softmax_rows", unnormalised)
+    assert not _pins_pass()
+    monkeypatch.setattr(oa, "_softmax_rows", real_soft)
+
+    monkeypatch.setattr(oa, "decode_bf16_bits",
+                        lambda b: (np.asarray(b).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64))
+    assert not _pins_pass()
+    monkeypatch.setattr(oa, "decode_bf16_bits", real_dec)
+
+    real_rows = oa.attention_rows_fp64
+
+    def transposed_kv(Qf, Kf, Vf, *a, **kw):
+        return real_rows(Qf, Vf, Kf, *a, **kw)
+    monkeypatch.setattr(oa, "attention_rows_fp64", transposed_kv)
+    assert not _pins_pass()
+
+    def no_scale(Qf, Kf, Vf, rows, scale, *a, **kw):
+        return real_rows(Qf, Kf, Vf, rows, 1.0, *a, **kw)
+    monkeypatch.setattr(oa, "attention_rows_fp64", no_scale)
+    assert not _pins_pass()
+    monkeypatch.setattr(oa, "attention_rows_fp64", real_rows)
+    assert _pins_pass()
