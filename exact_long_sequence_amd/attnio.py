@@ -1,0 +1,151 @@
+"""Thin Python binding of the attnio C ABI (argument marshalling only).
+
+Every function here has the name of the C entry point it calls.  torch is used
+only for device memory and the current HIP stream; every step of the attention
+computation runs in the gfx950 kernels of libattnio.so.  There is no fallback:
+if the library has not been built, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch  # imported first so that libattnio.so binds to torch's HIP runtime
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libattnio.so")
+_lib = None
+
+ATTN_OK = 0
+
+__all__ = ["attn_fwd", "attn_fwd_f32", "attn_strerror", "attn_version", "attn_query_tiling",
+           "attn_io_model", "library_path", "load_library"]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libattnio.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m exact_long_sequence_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("attn_fwd", "attn_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+        fn.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.attn_query_tiling.argtypes = [i32, i32, ip, ip, ip, ip]
+    lib.attn_query_tiling.restype = i32
+    lib.attn_io_model.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]
+    lib.attn_io_model.restype = i32
+    _lib = lib
+    return lib
+
+
+def attn_strerror(code: int) -> str:
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+def attn_query_tiling(d: int, causal: bool = False) -> dict:
+    lib = load_library()
+    vals = [ctypes.c_int(0) for _ in range(4)]
+    rc = lib.attn_query_tiling(int(d), int(bool(causal)), *[ctypes.byref(x) for x in vals])
+    if rc != ATTN_OK:
+        raise RuntimeError(attn_strerror(rc))
+    return dict(zip(("BM", "BN", "stages", "waves"), (x.value for x in vals)))
+
+
+def attn_io_model(B: int, H: int, N: int, d: int, elem_bytes: int, causal: bool,
+                  kv_len_host=None) -> dict:
+    """Host-side I/O model of one call (see include/attnio.h)."""
+    lib = load_library()
+    out = (ctypes.c_double * 5)()
+    kv_ptr = None
+    if kv_len_host is not None:
+        arr = (ctypes.c_int32 * B)(*[int(x) for x in kv_len_host])
+        kv_ptr = ctypes.cast(arr, ctypes.c_void_p)
+    rc = lib.attn_io_model(B, H, N, d, elem_bytes, int(bool(causal)), kv_ptr, out)
+    if rc != ATTN_OK:
+        raise RuntimeError(attn_strerror(rc))
+    return dict(zip(("t_min", "t_lds", "t_l2", "flops", "pairs"), list(out)))
+
+
+def _check(q, k, v, dtype):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out):
+    lib = load_library()
+    _check(q, k, v, dtype)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    kv_ptr = None
+    if kv_len is not None:
+        if not isinstance(kv_len, torch.Tensor):
+            kv_len = torch.tensor(kv_len, dtype=torch.int32)
+        if kv_len.device != q.device or kv_len.dtype != torch.int32:
+            kv_len = kv_len.to(device=q.device, dtype=torch.int32)
+        kv_len = kv_len.contiguous()
+        if kv_len.numel() != B:
+            raise ValueError(f"kv_len must have B={B} entries, got {kv_len.numel()}")
+        kv_ptr = kv_len.data_ptr()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   B, H, N, d, float(scale), int(bool(causal)), kv_ptr, stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"{fn_name}: {attn_strerror(rc)} (code {rc})")
+    return out
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 exact attention forward on [B, H, N, d] device tensors (d in {64, 128}).
+
+    kv_len: None or int32 [B] key-padding lengths (moved to the device if needed).
+    scale: defaults to 1/sqrt(d).  Enqueued on the current stream; no synchronisation."""
+    return _call("attn_fwd", torch.bfloat16, q, k, v, causal, kv_len, scale, out)
+
+
+def attn_fwd_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                 kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 exact attention forward; same contract as attn_fwd."""
+    return _call("attn_fwd_f32", torch.float32, q, k, v, causal, kv_len, scale, out)

@@ -1,0 +1,175 @@
+// Exact attention forward in fp32 end to end (gfx950, vector ALU).
+//
+// Same streamed schedule as the bf16 path (load a Q tile, stream K/V tiles,
+// partial scores, online softmax update, accumulate: "From Attention Graph to
+// FlashAttention - A Memory-Centric Compilation Approach in AICF", section 3),
+// but every product, exponential and sum is binary32 with no narrower
+// intermediate.  This path serves small fp32 problems, which are bound by
+// latency rather than throughput, so it trades MFMA for parallelism over keys:
+//
+//   workgroup = 256 threads = 16 queries x 16 key lanes
+//   each thread runs its own online softmax over keys j = 16*t + lane of every
+//   64-key LDS tile, with its own (m, l, acc[d]) state;
+//   the 16 partial states of a query are merged at the end with the same
+//   rescale the online update uses (the streaming reduction merges exactly:
+//   "IO-Aware Algorithms", How it works, online softmax).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace attnio {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQ = 16;        // queries per workgroup
+constexpr int kLanes = 16;    // key lanes per query
+constexpr int kBN = 64;       // keys per LDS tile
+
+template <int D, bool CAUSAL, bool NEG>
+__global__ __launch_bounds__(256)
+void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                         const float* __restrict__ V, float* __restrict__ O,
+                         const int32_t* __restrict__ kv_len, int H, int N, float c,
+                         int n_qtiles) {
+  constexpr int P = D + 4;  // padded LDS row (floats): keeps 16 rows on distinct banks
+  __shared__ __attribute__((aligned(16))) float qs[kQ * P];
+  __shared__ __attribute__((aligned(16))) float ks[kBN * P];
+  __shared__ __attribute__((aligned(16))) float vs[kBN * P];
+
+  const int tid = threadIdx.x;
+  const int qi = tid / kLanes;
+  const int kl = tid % kLanes;
+
+  const int bh = blockIdx.x / n_qtiles;
+  int qt = blockIdx.x % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int b = bh / H;
+  int L = N;
+  if (kv_len != nullptr) {
+    L = kv_len[b];
+    L = L < 0 ? 0 : (L > N ? N : L);
+  }
+  const int q0 = qt * kQ;
+  int kend = L;
+  if (CAUSAL) kend = min(kend, min(N, q0 + kQ));
+
+  const size_t slice = (size_t)bh * N * D;
+  const float* Qs = Q + slice;
+  const float* Ks = K + slice;
+  const float* Vs = V + slice;
+  float* Os = O + slice;
+
+  for (int e = tid; e < kQ * D / 4; e += 256) {
+    const int r = e / (D / 4), c4 = e % (D / 4);
+    const int gr = min(q0 + r, N - 1);
+    *(float4*)&qs[r * P + c4 * 4] = *(const float4*)&Qs[(size_t)gr * D + c4 * 4];
+  }
+
+  const int qrow = q0 + qi;
+  float m = NEG ? INFINITY : -INFINITY;  // running extreme of the raw scores
+  float l = 0.f;
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
+
+  for (int j0 = 0; j0 < kend; j0 += kBN) {
+    __syncthreads();
+    for (int e = tid; e < kBN * D / 4; e += 256) {
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      const int gr = min(j0 + r, kend - 1);
+      *(float4*)&ks[r * P + c4 * 4] = *(const float4*)&Ks[(size_t)gr * D + c4 * 4];
+      *(float4*)&vs[r * P + c4 * 4] = *(const float4*)&Vs[(size_t)gr * D + c4 * 4];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int t = 0; t < kBN / kLanes; ++t) {
+      const int jl = t * kLanes + kl;
+      const int key = j0 + jl;
+      bool ok = key < kend;
+      if (CAUSAL) ok = ok && key <= qrow;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; e += 4) {
+        const float4 a = *(const float4*)&qs[qi * P + e];
+        const float4 k4 = *(const float4*)&ks[jl * P + e];
+        s = __builtin_fmaf(a.x, k4.x, s);
+        s = __builtin_fmaf(a.y, k4.y, s);
+        s = __builtin_fmaf(a.z, k4.z, s);
+        s = __builtin_fmaf(a.w, k4.w, s);
+      }
+      if (!ok) continue;
+      // online update with the raw-score extreme m; weights exp2((s - m) * c)
+      const float m_new = NEG ? fminf(m, s) : fmaxf(m, s);
+      const float alpha = (m == m_new) ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
+      const float p = __builtin_amdgcn_exp2f((s - m_new) * c);
+      l = l * alpha + p;
+#pragma unroll
+      for (int e = 0; e < D; e += 4) {
+        const float4 v4 = *(const float4*)&vs[jl * P + e];
+        acc[e + 0] = __builtin_fmaf(p, v4.x, acc[e + 0] * alpha);
+        acc[e + 1] = __builtin_fmaf(p, v4.y, acc[e + 1] * alpha);
+        acc[e + 2] = __builtin_fmaf(p, v4.z, acc[e + 2] * alpha);
+        acc[e + 3] = __builtin_fmaf(p, v4.w, acc[e + 3] * alpha);
+      }
+      m = m_new;
+    }
+  }
+
+  // merge the 16 key-lane states of each query (lanes 16*q .. 16*q+15 of a wave)
+  float m_all = m;
+#pragma unroll
+  for (int off = kLanes / 2; off > 0; off /= 2) {
+    const float o = __shfl_xor(m_all, off, kLanes);
+    m_all = NEG ? fminf(m_all, o) : fmaxf(m_all, o);
+  }
+  const bool empty = NEG ? (m_all == INFINITY) : (m_all == -INFINITY);
+  const bool mine_empty = NEG ? (m == INFINITY) : (m == -INFINITY);
+  const float w = (empty || mine_empty) ? 0.f : __builtin_amdgcn_exp2f((m - m_all) * c);
+  l *= w;
+#pragma unroll
+  for (int off = kLanes / 2; off > 0; off /= 2) l += __shfl_xor(l, off, kLanes);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    float x = acc[e] * w;
+#pragma unroll
+    for (int off = kLanes / 2; off > 0; off /= 2) x += __shfl_xor(x, off, kLanes);
+    acc[e] = x;
+  }
+  if (qrow < N) {
+    constexpr int PER = D / kLanes;
+#pragma unroll
+    for (int e = 0; e < D; ++e)
+      if (e / PER == kl) Os[(size_t)qrow * D + e] = acc[e] * inv;
+  }
+}
+
+template <int D, bool CAUSAL, bool NEG>
+hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+  const int n_qtiles = (a.N + kQ - 1) / kQ;
+  const long long grid = (long long)a.B * a.H * n_qtiles;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
+                     a.kv_len, a.H, a.N, a.scale * kLog2e, n_qtiles);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch(const FwdArgs& a, hipStream_t stream) {
+  const bool neg = a.scale < 0.f;
+  if (a.causal) return neg ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
+  return neg ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 64) return dispatch<64>(a, stream);
+  if (a.d == 128) return dispatch<128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attnio

@@ -1,0 +1,192 @@
+// C-ABI front end of the attention library: argument checks, device check,
+// kernel selection and the host-side I/O model.  See include/attnio.h for the
+// contract of every entry point.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/attnio.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxDevices = 64;
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("ATTNIO_LOG");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+// 1 = gfx950, 0 = other, -1 = not yet probed.
+int g_dev_ok[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+bool current_device_is_gfx950() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t p;
+    g_dev_ok[dev] = 0;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess && strncmp(p.gcnArchName, "gfx950", 6) == 0)
+      g_dev_ok[dev] = 1;
+  });
+  return g_dev_ok[dev] == 1;
+}
+
+bool overlaps(const void* a, const void* b, size_t bytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bytes && y < x + bytes;
+}
+
+int validate(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+             float scale, int elem) {
+  if (!Q || !K || !V || !O) return ATTN_E_NULL;
+  if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
+  if (B < 1 || H < 1 || N < 1) return ATTN_E_SHAPE;
+  const long long total = (long long)B * H * N * d;
+  if (total >= (1LL << 31)) return ATTN_E_SHAPE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return ATTN_E_ALIGN;
+  const size_t bytes = (size_t)total * elem;
+  if (overlaps(O, Q, bytes) || overlaps(O, K, bytes) || overlaps(O, V, bytes)) return ATTN_E_ALIAS;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return ATTN_E_ARG;
+  return ATTN_OK;
+}
+
+int run(bool bf16, const void* Q, const void* K, const void* V, void* O, int B, int H, int N,
+        int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+  const int rc = validate(Q, K, V, O, B, H, N, d, scale, bf16 ? 2 : 4);
+  if (rc != ATTN_OK) return rc;
+  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  attnio::FwdArgs a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0};
+  if (log_enabled()) {
+    attnio::Tiling t{};
+    if (bf16 && attnio::bf16_tiling(d, causal, &t))
+      fprintf(stderr, "[attnio] bf16 B=%d H=%d N=%d d=%d causal=%d kv_len=%s BM=%d BN=%d stages=%d waves=%d lds=%d\n",
+              B, H, N, d, causal, kv_len ? "dev" : "none", t.BM, t.BN, t.stages, t.waves, t.lds_bytes);
+    else
+      fprintf(stderr, "[attnio] f32 B=%d H=%d N=%d d=%d causal=%d kv_len=%s\n", B, H, N, d, causal,
+              kv_len ? "dev" : "none");
+  }
+  const hipError_t e = bf16 ? attnio::launch_fwd_bf16(a, (hipStream_t)stream)
+                            : attnio::launch_fwd_f32(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (log_enabled()) fprintf(stderr, "[attnio] launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+// number of (query, visible key) pairs of one (b, h) slice
+double pair_count(long long N, long long L, bool causal) {
+  if (!causal) return (double)N * (double)L;
+  // sum_i min(i + 1, L) = L(L+1)/2 + (N - L) L
+  return (double)L * (double)(L + 1) / 2.0 + (double)(N - L) * (double)L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+             float scale, int causal, const int32_t* kv_len, void* stream) {
+  return run(true, Q, K, V, O, B, H, N, d, scale, causal, kv_len, stream);
+}
+
+int attn_fwd_f32(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                 float scale, int causal, const int32_t* kv_len, void* stream) {
+  return run(false, Q, K, V, O, B, H, N, d, scale, causal, kv_len, stream);
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_HEAD_DIM: return "unsupported head size d (supported: 64, 128)";
+    case ATTN_E_SHAPE: return "bad shape: B, H, N must be >= 1 and B*H*N*d < 2^31";
+    case ATTN_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case ATTN_E_LAUNCH: return "kernel launch failed";
+    case ATTN_E_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+    case ATTN_E_ALIAS: return "O overlaps Q, K or V";
+    case ATTN_E_ARG: return "argument out of range (scale must be finite)";
+    default: return "unknown attnio status code";
+  }
+}
+
+int attn_version(void) { return kVersion; }
+
+int attn_query_tiling(int d, int causal, int* BM, int* BN, int* stages, int* waves) {
+  attnio::Tiling t{};
+  if (!attnio::bf16_tiling(d, causal, &t)) return ATTN_E_HEAD_DIM;
+  if (BM) *BM = t.BM;
+  if (BN) *BN = t.BN;
+  if (stages) *stages = t.stages;
+  if (waves) *waves = t.waves;
+  return ATTN_OK;
+}
+
+int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
+                  const int32_t* kv_len_host, double out[5]) {
+  if (!out) return ATTN_E_NULL;
+  if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
+  if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
+  if (elem_bytes != 2 && elem_bytes != 4) return ATTN_E_ARG;
+  attnio::Tiling t{};
+  attnio::bf16_tiling(d, causal, &t);
+  const double row = (double)d * elem_bytes;
+  const long long BM = t.BM, BN = t.BN;
+  const long long nqt = (N + BM - 1) / BM;
+  // query tiles of one head resident together on one XCD (32 CUs); the
+  // workgroups per CU follow from the LDS budget of 160 KiB and two waves
+  // per SIMD.
+  const long long wg_per_cu_lds = (160 * 1024) / (t.lds_bytes > 0 ? t.lds_bytes : 1);
+  const long long wg_per_cu_waves = (4 * (d == 64 ? 4 : 2)) / t.waves;
+  const long long wg_per_cu = wg_per_cu_lds < wg_per_cu_waves ? wg_per_cu_lds : wg_per_cu_waves;
+  const long long resident = 32 * (wg_per_cu > 0 ? wg_per_cu : 1);
+  double t_min = 4.0 * B, t_lds = 0, t_l2 = 0, pairs = 0;
+  for (int b = 0; b < B; ++b) {
+    long long L = N;
+    if (kv_len_host) {
+      L = kv_len_host[b];
+      L = L < 0 ? 0 : (L > N ? N : L);
+    }
+    const double p = pair_count(N, L, causal != 0);
+    for (int h = 0; h < H; ++h) {
+      pairs += p;
+      t_min += row * (2.0 * N + 2.0 * L);
+      t_l2 += row * 2.0 * N;  // Q read and O written once
+      for (long long qt = 0; qt < nqt; ++qt) {
+        long long kend = L;
+        if (causal) kend = kend < (qt + 1) * BM ? kend : ((qt + 1) * BM < N ? (qt + 1) * BM : N);
+        const long long tiles = (kend + BN - 1) / BN;
+        t_lds += row * (double)BM + 2.0 * row * (double)(tiles * BN);
+      }
+      // one generation = `resident` query tiles running together; K/V of the
+      // keys that generation needs come from HBM once per generation
+      for (long long g0 = 0; g0 < nqt; g0 += resident) {
+        // causal tiles run longest first: generation g covers the highest
+        // remaining query tiles, so it needs keys up to its first tile's end
+        const long long top = causal ? nqt - g0 : nqt;
+        long long kend = L;
+        if (causal) kend = kend < top * BM ? kend : (top * BM < N ? top * BM : N);
+        t_l2 += 2.0 * row * (double)kend;
+      }
+    }
+  }
+  out[0] = t_min;
+  out[1] = t_lds;
+  out[2] = t_l2;
+  out[3] = 4.0 * d * pairs;
+  out[4] = pairs;
+  return ATTN_OK;
+}
+
+}  // extern "C"

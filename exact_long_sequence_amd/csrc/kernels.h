@@ -1,0 +1,35 @@
+// Internal launcher declarations shared by the C-ABI front end and the kernel
+// translation units.  Not part of the public interface (see include/attnio.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnio {
+
+// Launch parameters common to both precisions.  All pointers are device
+// pointers already validated by the front end.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* kv_len;  // device int32[B] or nullptr
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
+// Tile configuration of the bf16 streaming kernel for head size d.
+struct Tiling {
+  int BM;      // query rows resident per workgroup
+  int BN;      // keys per streamed K/V tile
+  int stages;  // K/V LDS buffers
+  int waves;   // wavefronts per workgroup (32 query rows each)
+  int lds_bytes;
+};
+
+bool bf16_tiling(int d, int causal, Tiling* t);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+}  // namespace attnio

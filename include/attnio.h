@@ -1,0 +1,108 @@
+/*
+ * attnio -- exact long-sequence self-attention forward for AMD Instinct MI355X
+ * (gfx950), as a plain C ABI.
+ *
+ * The operation is exact attention, O = softmax(scale * Q K^T + mask) V, the
+ * operator graph "Scores = Q x K^T; Mask; Softmax; Output = Scores x V" of
+ * "From Attention Graph to FlashAttention - A Memory-Centric Compilation
+ * Approach in AICF" (section 1), computed by the streamed schedule of its
+ * section 3 (load a Q tile, stream K/V tiles, partial scores, online softmax
+ * update, accumulate) so that no N x N intermediate ever reaches memory.  The
+ * call plays the role of the special-kernel library entry flash_attention(Q, K,
+ * V) of that page's section 4.  Tiling follows the I/O analysis of
+ * tall-and-skinny products of "I/O Analysis is All You Need: An I/O Analysis
+ * for Long-Sequence Attention" (abstract: I/O-optimal tiling and scheduling,
+ * overlap of communication with computation, parallel softmax).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout      Q, K, V, O are contiguous row-major [B, H, N, d] tensors (d is
+ *             innermost) in device memory, all of one element type.  O must not
+ *             overlap Q, K or V.  Pointers must be 16-byte aligned.
+ * d           64 or 128.
+ * N           any N >= 1; B, H >= 1; B*H*N*d must be < 2^31.
+ * scale       multiplies Q K^T; taken as given (not derived from d).
+ * causal      nonzero: query i may attend to key j only if j <= i.
+ * kv_len      NULL, or a DEVICE pointer to int32[B]: keys j >= kv_len[b] of
+ *             batch b are masked (key padding).  Values are clamped to [0, N]
+ *             on the device.  Every query row is still produced; a row with no
+ *             visible key (kv_len[b] == 0) is written as zeros.
+ * stream      a hipStream_t passed as an opaque pointer (NULL: default stream).
+ *             The call only enqueues work: it never synchronises, allocates
+ *             nothing and keeps no state between calls; device-side faults
+ *             surface at the caller's next synchronisation.
+ * Ownership   the caller owns every buffer.
+ * Errors      0 on success, a negative ATTN_E* code otherwise.  Arguments are
+ *             checked on the host before anything is enqueued; on an error
+ *             nothing is enqueued and O is untouched.  attn_strerror() names
+ *             each code.  Nothing prints unless ATTNIO_LOG=1 is set.
+ */
+#ifndef ATTNIO_H
+#define ATTNIO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,      /* a required pointer is NULL */
+  ATTN_E_HEAD_DIM = -2,  /* d is not 64 or 128 */
+  ATTN_E_SHAPE = -3,     /* B, H or N < 1, or B*H*N*d >= 2^31 */
+  ATTN_E_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned */
+  ATTN_E_LAUNCH = -5,    /* the kernel launch was rejected by the HIP runtime */
+  ATTN_E_DEVICE = -6,    /* the current device is not a gfx950 GPU */
+  ATTN_E_ALIAS = -7,     /* O overlaps Q, K or V */
+  ATTN_E_ARG = -8        /* another argument is out of range */
+};
+
+/* bf16 attention forward: Q, K, V, O hold bfloat16 values.  Products run on
+ * bf16 matrix cores with fp32 accumulation; softmax statistics are fp32; the
+ * probabilities are rounded to bf16 (round-to-nearest-even) before the P x V
+ * product and the row sum is taken over those rounded values; O is rounded to
+ * bf16 once, at the end. */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O,
+             int B, int H, int N, int d, float scale, int causal,
+             const int32_t* kv_len, void* stream);
+
+/* fp32 attention forward: Q, K, V, O hold IEEE binary32 values, and every
+ * step runs in fp32 with no narrower intermediate. */
+int attn_fwd_f32(const void* Q, const void* K, const void* V, void* O,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const int32_t* kv_len, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* attn_strerror(int code);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+/* Tile configuration the bf16 path uses for head size d (1 = causal): rows of
+ * the resident query tile (BM), keys per streamed K/V tile (BN), K/V LDS stages
+ * and waves per workgroup.  Host only.  Returns 0 or ATTN_E_HEAD_DIM.  Any
+ * output pointer may be NULL. */
+int attn_query_tiling(int d, int causal, int* BM, int* BN, int* stages, int* waves);
+
+/* I/O model of one call (host only; kv_len_host is a HOST int32[B] or NULL).
+ * Fills, in bytes:
+ *   out[0] t_min   compulsory HBM traffic: Q, K, V read once, O written once
+ *                  (keys past kv_len are never read), plus 4*B bytes of kv_len;
+ *   out[1] t_lds   bytes streamed into LDS by the chosen tiling (Q once per
+ *                  query tile, K/V once per query tile for every key tile the
+ *                  tile visits) -- the L2->LDS traffic of the tall-skinny
+ *                  products, which shrinks as 1/BM;
+ *   out[2] t_l2    predicted L2-miss traffic when the query tiles of one head
+ *                  run together on one XCD and share its L2;
+ *   out[3] flops   algorithmic FLOPs, 4*d per (query, visible key) pair;
+ *   out[4] pairs   number of (query, visible key) pairs (one exp each).
+ * Returns 0, or a negative code for invalid shapes. */
+int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
+                  const int32_t* kv_len_host, double out[5]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNIO_H */

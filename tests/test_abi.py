@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/attnio.h declares, and rejects bad arguments on the host before
+any device call.  The I/O model is checked against its closed forms."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_long_sequence_amd import attnio
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnio.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attnio.library_path()):
+        pytest.fail("libattnio.so is not built (run python -m exact_long_sequence_amd.build)")
+    return attnio.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"attn_fwd", "attn_fwd_f32", "attn_strerror", "attn_version", "attn_query_tiling",
+            "attn_io_model"} <= names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in attnio.h but not exported"
+
+
+def test_strerror_and_version(lib):
+    assert attnio.attn_version() >= 100
+    for code in range(0, -9, -1):
+        s = attnio.attn_strerror(code)
+        assert s and "unknown" not in s
+    assert "unknown" in attnio.attn_strerror(-99)
+
+
+def test_query_tiling():
+    for d in (64, 128):
+        t = attnio.attn_query_tiling(d, False)
+        assert t["BM"] % 32 == 0 and t["BN"] % 32 == 0 and t["stages"] >= 2
+        assert t["BM"] == 32 * t["waves"]
+        # K and V stages of BN x d bf16 rows fit the 160 KiB LDS of a gfx950 CU
+        assert t["stages"] * 2 * t["BN"] * d * 2 <= 160 * 1024
+    with pytest.raises(RuntimeError):
+        attnio.attn_query_tiling(96, False)
+
+
+def _call(lib, name, q=0x1000, k=0x2000000, v=0x4000000, o=0x6000000, B=1, H=1, N=16, d=64,
+          scale=0.125, causal=0):
+    fn = getattr(lib, name)
+    return fn(q, k, v, o, B, H, N, d, ctypes.c_float(scale), causal, None, None)
+
+
+@pytest.mark.parametrize("name", ["attn_fwd", "attn_fwd_f32"])
+def test_host_side_argument_errors(lib, name):
+    assert _call(lib, name, q=None) == -1
+    assert _call(lib, name, o=None) == -1
+    assert _call(lib, name, d=96) == -2
+    assert _call(lib, name, d=0) == -2
+    assert _call(lib, name, N=0) == -3
+    assert _call(lib, name, B=-1) == -3
+    assert _call(lib, name, B=1 << 12, H=1 << 12, N=1 << 12, d=64) == -3  # >= 2^31 elements
+    assert _call(lib, name, q=0x1008) == -4
+    assert _call(lib, name, o=0x1000 + 64) == -7  # O overlaps Q
+    assert _call(lib, name, scale=float("nan")) == -8
+    assert _call(lib, name, scale=float("inf")) == -8
+
+
+def test_no_gpu_reports_device_error(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _call(lib, "attn_fwd") == -6
+
+
+def test_io_model_closed_forms():
+    B, H, N, d = 1, 2, 1000, 128
+    m = attnio.attn_io_model(B, H, N, d, 2, False)
+    assert m["t_min"] == 4 * B + 2 * d * H * (2 * N + 2 * N)
+    assert m["pairs"] == H * N * N
+    assert m["flops"] == 4 * d * H * N * N
+    c = attnio.attn_io_model(B, H, N, d, 2, True)
+    assert c["pairs"] == H * N * (N + 1) // 2
+    # key padding: K and V are read only up to kv_len; pairs = N * L (non-causal)
+    p = attnio.attn_io_model(2, 1, 64, 64, 2, False, [10, 64])
+    assert p["t_min"] == 8 + 2 * 64 * (2 * 64 + 2 * 10) + 2 * 64 * (2 * 64 + 2 * 64)
+    assert p["pairs"] == 64 * 10 + 64 * 64
+    # causal with padding: sum_i min(i + 1, L)
+    cp = attnio.attn_io_model(1, 1, 100, 64, 2, True, [30])
+    assert cp["pairs"] == sum(min(i + 1, 30) for i in range(100))
+    # L2->LDS traffic shrinks with the resident tile and exceeds the compulsory bytes
+    assert m["t_lds"] >= m["t_min"] - 4 * B
+    t = attnio.attn_query_tiling(d)
+    nqt = math.ceil(N / t["BM"])
+    ntile = math.ceil(N / t["BN"])
+    assert m["t_lds"] == H * nqt * (t["BM"] * d * 2 + 2 * ntile * t["BN"] * d * 2)
+    with pytest.raises(RuntimeError):
+        attnio.attn_io_model(1, 1, 10, 72, 2, False)
