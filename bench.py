@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one call of the fused bf16 kernel over the whole workload (every
+head, every query row), inputs already resident in HBM.  Default workload: the
+causal long-sequence case B=1, H=32, N=32768, d=128 (seeded N(0,1) inputs).
+
+Prints ONE JSON line with the throughput in algorithmic TFLOP/s (4*d FLOPs per
+(query, visible key) pair, i.e. 4*N^2*d per head halved for causal), the
+roofline position of the kernel (timed live with HIP events on the launch
+stream), the HBM traffic measured by rocprofv3 counters when a matching
+counter summary is committed under profiles/, and the fp64 CPU oracle timed on
+a bounded row sample on the host cores (which also checks those rows).
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (no sparsity)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+DEFAULT_WORKLOAD = "bf16_causal_h32_n32k_d128"
+KERNEL_SOURCE = os.path.join(ROOT, "exact_long_sequence_amd", "csrc", "attn_fwd_bf16.hip")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_h32_n32k_d128_counters.md")
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when it is
+    missing, for another workload, or taken on a different kernel source."""
+    if workload != DEFAULT_WORKLOAD or not os.path.exists(COUNTER_SUMMARY):
+        return None
+    text = open(COUNTER_SUMMARY).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+def copy_calibration(nbytes: int) -> None:
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, q, k, v, kv_len, out, budget_s: float):
+    """Time the fp64 oracle on a bounded seeded sample of query rows and check
+    those rows against the GPU output."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_long_sequence_amd.inputs import oracle_view, sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    kl = None if kv_len is None else kv_len.numpy()
+    rows = sample_rows(w.B, w.H, w.N, 65536, w.seed, kv_len=kl)
+    rng = np.random.default_rng(w.seed + 2)
+    rows = rows[rng.permutation(rows.size)]
+    qv, kv_, vv = oracle_view(q), oracle_view(k), oracle_view(v)
+    kind = "bf16" if w.dtype == "bf16" else "f32"
+    L = oracle.effective_kv_len(kl, w.B, w.N)
+    done, flops, max_err, sum_err, n_el = 0, 0.0, 0.0, 0.0, 0
+    t0 = time.perf_counter()
+    # a first small call gives the rate; later calls fill the time budget
+    n = 256
+    while done < rows.size:
+        elapsed = time.perf_counter() - t0
+        if done:
+            if elapsed >= budget_s:
+                break
+            rate = done / elapsed
+            n = int(min(rows.size - done, max(256.0, 0.95 * (budget_s - elapsed) * rate)))
+        r = rows[done:done + n]
+        want = oracle.attention_fp64(qv, kv_, vv, w.scale, w.causal, kl, kind=kind, rows=r)
+        i = r % w.N
+        Lr = L[(r // w.N) // w.H]
+        keys = np.minimum(i + 1, Lr) if w.causal else Lr
+        flops += 4.0 * w.d * float(keys.sum())
+        idx = torch.as_tensor(r, device=out.device, dtype=torch.long)
+        got = out.reshape(-1, w.d).index_select(0, idx).float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - want)
+        max_err = max(max_err, float(err.max()))
+        sum_err += float(err.sum())
+        n_el += err.size
+        done += r.size
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads if blas_threads else cores,
+        "kind": "oracle",
+        "sample": f"{done} seeded query rows of {w.name} (all keys each row sees), fp64 numpy, "
+                  f"{dt:.1f} s on {cores} visible host cores",
+        "seconds": dt,
+        "rows": int(done),
+        "parity_on_sample": {"max_abs_err": max_err, "mean_abs_err": sum_err / max(n_el, 1)},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: every box of this setup has a single MI355X and the "
+              "attention path here is the single-GPU share; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return 0
+
+    from exact_long_sequence_amd import attnio
+    from exact_long_sequence_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v, kv_len = workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    kvd = None if kv_len is None else kv_len.to(dev)
+    out = torch.empty_like(qd)
+    fn = attnio.attn_fwd if w.dtype == "bf16" else attnio.attn_fwd_f32
+    model = attnio.attn_io_model(w.B, w.H, w.N, w.d, 2 if w.dtype == "bf16" else 4, w.causal,
+                                 None if kv_len is None else kv_len.tolist())
+    tiling = attnio.attn_query_tiling(w.d, w.causal)
+
+    for _ in range(args.warmup):
+        fn(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fn(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale, out=out)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+
+    flops = model["flops"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
+    traffic = committed_traffic(w.name)
+    result = {
+        "metric": "attention fwd TFLOP/s (algorithmic 4*d per visible query-key pair)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": w.describe(),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": tflops / peak,
+            "traffic": traffic,
+        },
+        "io": {
+            "t_min_bytes": model["t_min"],
+            "t_l2_model_bytes": model["t_l2"],
+            "t_lds_model_bytes": model["t_lds"],
+            "traffic_over_t_min": None if traffic is None else traffic / model["t_min"],
+            "t_min_rate_GBs": model["t_min"] / (ms * 1e-3) / 1e9,
+            "hbm_peak_GBs": HBM_PEAK_GBS,
+        },
+        "tiling": tiling,
+        "kernel_source_sha256_16": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, kv_len, out, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
