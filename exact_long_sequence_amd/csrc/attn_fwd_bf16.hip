@@ -56,16 +56,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTauLog2 = 8.0f;  // lazy-rescale threshold (probabilities <= 2^8)
 
-template <int D, int BN, int WAVES>
+template <int D, int BN, int WAVES, int QB, int NSTAGES>
 struct Cfg {
-  static constexpr int BM = 32 * WAVES;
+  static constexpr int BM = 32 * QB * WAVES;              // query rows per workgroup
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per row
   static constexpr int ROWS_PER_256 = 256 / ROW_BYTES;   // rows sharing one 256 B bank line
   static constexpr int TILE_BYTES = BN * ROW_BYTES;      // one K or one V tile
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // K + V
-  static constexpr int STAGES = 2;
+  static constexpr int STAGES = NSTAGES;                 // K+V tiles resident in the LDS ring
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int LOADS = TILE_BYTES / 16 / THREADS;  // 16 B loads per thread per tensor
   static_assert(TILE_BYTES % (16 * THREADS) == 0, "tile must split evenly over threads");
@@ -93,21 +93,310 @@ __device__ __forceinline__ u32x2 swap_halves(float x) {
   return out;
 }
 
-template <int D, int BN, int WAVES, bool CAUSAL, bool NEG_SCALE>
-__global__ __launch_bounds__(64 * WAVES, 2)
+// One direct-to-LDS load of 16 bytes per lane: lane i of the wave writes LDS
+// bytes [lds + 16 i, lds + 16 i + 16) with the 16 bytes at gbase + voff.  It is
+// issued as inline assembly so that the compiler does not treat it as an LDS
+// store it must wait for before every LDS read of the other stages: completion
+// is awaited explicitly (s_waitcnt vmcnt) before the workgroup barrier that
+// hands a stage over.  M0 carries the wave-uniform LDS address.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// wait until at most N tile DMAs of this wave are still in flight
+template <int N>
+__device__ __forceinline__ void wait_dma_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ----------------------------------------------------------------------------
+// Per-tile building blocks.  A wave owns QB blocks of 32 query rows; lane
+// (h, c) owns query c of every block.  Every K or V operand read from LDS feeds
+// QB MFMAs, so LDS traffic per MFMA falls as 1/QB.  The blocks are
+// force-inlined so that the main loop can interleave the MFMA chain of one
+// tile with the softmax VALU work of another inside one basic block.
+// ----------------------------------------------------------------------------
+
+// S^T (BN keys x 32 queries, per query block) = K_tile Q^T
+template <class C, int D, int BN, int QB>
+__device__ __forceinline__ void qk_tile(const char LDS_AS* kl, const bf16x8 (&qf)[QB][D / 16],
+                                        f32x16 (&s)[QB][BN / 32], int col, int half) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      const int row = kb * 32 + col;
+      const int ch = (2 * ks + half) ^ swz_k<C>(row);
+      const bf16x8 a = *(const bf16x8 LDS_AS*)(kl + row * C::ROW_BYTES + ch * 16);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
+    }
+  }
+}
+
+// Masked scores become -inf (or +inf when the scale is negative, so that they
+// still map to exp2(-inf) = 0).  Only diagonal and padding tiles call this.
+template <int BN, int QB, bool CAUSAL, bool NEG>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[QB][BN / 32], int j0, int L,
+                                          const int (&qrow)[QB], int half) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+        bool ok = key < L;
+        if (CAUSAL) ok = ok && (key <= qrow[qb]);
+        s[qb][kb][r] = ok ? s[qb][kb][r] : (NEG ? INFINITY : -INFINITY);
+      }
+}
+
+// Row extreme of the raw scores (max, or min for a negative scale), over the
+// lane's 16 values per block and the partner lane 32 apart.
+template <int BN, bool NEG>
+__device__ __forceinline__ float row_extreme(const f32x16 (&s)[BN / 32]) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = NEG ? fminf(mx, s[kb][r]) : fmaxf(mx, s[kb][r]);
+  const u32x2 pr = swap_halves(mx);
+  return NEG ? fminf(__uint_as_float(pr[0]), __uint_as_float(pr[1]))
+             : fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+// P = exp2(S*c - m) rounded to bf16 and packed as the B operands of the P x V
+// MFMA (operand i covers keys 16 i .. 16 i + 15 of the tile); the lane's
+// partial row sum accumulates the rounded values.
+template <int BN>
+__device__ __forceinline__ void softmax_p(const f32x16 (&s)[BN / 32], float c, float m_use,
+                                          bf16x8 (&pb)[BN / 16], float& l_run) {
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      bf16x8 p;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8)
+        p[t8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][sp * 8 + t8], c, -m_use));
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const bf16x2 pp = {p[2 * t2], p[2 * t2 + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+      }
+      pb[kb * 2 + sp] = p;
+    }
+}
+
+// O^T (D x 32 queries, per query block) += V_tile^T P^T.  The transpose read:
+// lane 16g + 4j + q supplies V row (16 st + 8u + 4h + j), columns
+// 32 db + 16 (g % 2) + 4 q .. +3, and lane 16g + i receives column
+// 32 db + 16 (g % 2) + i of those four rows, which is the A-operand layout
+// (d down the rows, keys along k).
+template <class C, int D, int BN, int QB>
+__device__ __forceinline__ void pv_tile(const char LDS_AS* vl, const bf16x8 (&pb)[QB][BN / 16],
+                                        f32x16 (&acc)[QB][D / 32], int lane, int half) {
+  const int g = lane / 16;
+  const int jr = (lane % 16) / 4;
+  const int qq = lane % 4;
+#pragma unroll
+  for (int st = 0; st < BN / 16; ++st) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      bf16x8 a;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = st * 16 + u * 8 + half * 4 + jr;
+        const int colb = (db * 32 + (g % 2) * 16 + qq * 4) * 2;  // byte offset in the row
+        const int ch = (colb / 16) ^ swz_v<C>(row);
+        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 LDS_AS*)(vl + row * C::ROW_BYTES + ch * 16 + (colb % 16)));
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][st], acc[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+// Prefetched variants: the LDS operands of round r+1 are read before the
+// MFMAs of round r are issued, and a scheduling barrier keeps the compiler
+// from sinking the reads next to their uses, so one round of MFMAs (BN/32 * QB
+// for S, D/32 * QB for O) covers the LDS latency of the next round's reads.
+template <class C, int D, int BN, int QB>
+__device__ __forceinline__ void qk_tile_pf(const char LDS_AS* kl, const bf16x8 (&qf)[QB][D / 16],
+                                           f32x16 (&s)[QB][BN / 32], int col, int half) {
+  constexpr int KB = BN / 32;
+  auto rd = [&](int ks, int kb) __attribute__((always_inline)) {
+    const int row = kb * 32 + col;
+    const int ch = (2 * ks + half) ^ swz_k<C>(row);
+    return *(const bf16x8 LDS_AS*)(kl + row * C::ROW_BYTES + ch * 16);
+  };
+  bf16x8 a[2][KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) a[0][kb] = rd(0, kb);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (ks + 1 < D / 16) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[(ks + 1) & 1][kb] = rd(ks + 1, kb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][kb], qf[qb][ks], s[qb][kb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <class C, int D, int BN, int QB>
+__device__ __forceinline__ void pv_tile_pf(const char LDS_AS* vl, const bf16x8 (&pb)[QB][BN / 16],
+                                           f32x16 (&acc)[QB][D / 32], int lane, int half) {
+  constexpr int DB = D / 32;
+  const int g = lane / 16;
+  const int jr = (lane % 16) / 4;
+  const int qq = lane % 4;
+  auto rd = [&](int st, int db) __attribute__((always_inline)) {
+    bf16x8 a;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = st * 16 + u * 8 + half * 4 + jr;
+      const int colb = (db * 32 + (g % 2) * 16 + qq * 4) * 2;
+      const int ch = (colb / 16) ^ swz_v<C>(row);
+      const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 LDS_AS*)(vl + row * C::ROW_BYTES + ch * 16 + (colb % 16)));
+      const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
+    }
+    return a;
+  };
+  bf16x8 a[2][DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) a[0][db] = rd(0, db);
+#pragma unroll
+  for (int st = 0; st < BN / 16; ++st) {
+    if (st + 1 < BN / 16) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) a[(st + 1) & 1][db] = rd(st + 1, db);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st & 1][db], pb[qb][st], acc[qb][db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Scheduling hints (LLVM AMDGPU sched_group_barrier masks): interleave one
+// MFMA with a few VALU instructions and an LDS read, so that the matrix core
+// stays busy while the softmax of the neighbouring tile runs.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+template <int N_MFMA, int VALU_PER, int DS_EVERY, int DS_AHEAD>
+__device__ __forceinline__ void interleave_hint() {
+  if (DS_AHEAD > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, DS_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (DS_EVERY > 0 && i % DS_EVERY == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if (VALU_PER > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU_PER, 0);
+  }
+}
+
+#ifndef ATTNIO_HINT_VALU
+#define ATTNIO_HINT_VALU 4
+#endif
+#ifndef ATTNIO_PRIO
+#define ATTNIO_PRIO 1
+#endif
+#ifndef ATTNIO_PF
+#define ATTNIO_PF 0
+#endif
+#ifndef ATTNIO_SEQ_HINT
+#define ATTNIO_SEQ_HINT 0
+#endif
+#ifndef ATTNIO_DS_AHEAD
+#define ATTNIO_DS_AHEAD 4
+#endif
+
+// Sequential form: keep LDS operand reads ATTNIO_DS_AHEAD instructions ahead
+// of the MFMAs that consume them (K reads: one per QB MFMAs; V transpose
+// reads: two per QB MFMAs).
+template <int N_READS, int QB>
+__device__ __forceinline__ void seq_qk_hint() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, ATTNIO_DS_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N_READS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, QB, 0);
+    if (i + ATTNIO_DS_AHEAD < N_READS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+}
+template <int N_OPS, int QB>
+__device__ __forceinline__ void seq_pv_hint() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * ATTNIO_DS_AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N_OPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, QB, 0);
+    if (i + ATTNIO_DS_AHEAD < N_OPS) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// The kernel.  Two loop forms share the building blocks:
+//  * sequential (OVERLAP = false): per tile, S = K Q^T, mask, softmax, O += V^T P^T,
+//    over an LDS ring of STAGES (K, V) tile pairs with tile t + STAGES - 1 in
+//    flight while tile t is computed;
+//  * pipelined (OVERLAP = true): per wave and tile t, two interleaved phases
+//      A: S(t+1) = K(t+1) Q^T on MFMA   ||  P(t) = exp2(S(t) c - m), row sums
+//      B: O += V(t)^T P(t)^T on MFMA     ||  mask, row max and shift update of S(t+1)
+//    with K one tile ahead of V in a 2 + 2 stage ring.
+// Both are the three-level overlap: HBM/L2 -> LDS by DMA of later tiles,
+// LDS -> VGPR operand reads under the MFMA chains, MFMA under VALU softmax.
+// ----------------------------------------------------------------------------
+template <int D, int BN, int WAVES, int QB, int STAGES, int MODE, bool CAUSAL, bool NEG_SCALE>
+__global__ __launch_bounds__(64 * WAVES, QB == 1 ? 2 : 1)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                           const int32_t* __restrict__ kv_len, int H, int N, float c,
                           int n_qtiles) {
-  using C = Cfg<D, BN, WAVES>;
+  using C = Cfg<D, BN, WAVES, QB, MODE == 0 ? STAGES : 2>;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
   const int lane = tid % 64;
   const int half = lane / 32;   // h
-  const int col = lane % 32;    // c: the query this lane owns
+  const int col = lane % 32;    // c: the query this lane owns in each block
 
   // ---- logical tile id: XCD-aware remap, then (batch*head, query tile) ----
   const int G = gridDim.x;
@@ -124,6 +413,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     L = kv_len[b];
     L = L < 0 ? 0 : (L > N ? N : L);
   }
+  L = __builtin_amdgcn_readfirstlane(L);
   const int q0 = qt * C::BM;
   int kend = L;
   if (CAUSAL) kend = min(kend, min(N, q0 + C::BM));
@@ -134,230 +424,390 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const char* Kg = (const char*)(K + slice);
   const char* Vg = (const char*)(V + slice);
   __bf16* Os = O + slice;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
-  // ---- K/V tile loader (direct to LDS) ----
-  auto issue_tile = [&](int t, int stage) {
+  // DMA of K or V tile t into LDS byte offset `dst` of the ring.  Load i of a
+  // lane fills LDS bytes pos = (i*THREADS + 64*wave + lane)*16 of the tile,
+  // i.e. row pos / ROW_BYTES and physical chunk (pos % ROW_BYTES) / 16; the
+  // lane fetches the logical chunk that the swizzle stores there.  A tail tile
+  // clamps rows >= kend to kend - 1 (masked keys: they only need to be finite
+  // memory inside the tensor).
+  auto issue = [&](const char* gsrc, bool is_v, int t, uint32_t dst) __attribute__((always_inline)) {
     const int j0 = t * BN;
-    char LDS_AS* kl = smem + stage * C::STAGE_BYTES;
-    char LDS_AS* vl = kl + C::TILE_BYTES;
+    const char* gt = gsrc + (size_t)j0 * C::ROW_BYTES;
+    const int last = kend - 1 - j0;  // last valid row of this tile
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int wbase = (i * C::THREADS + wave * 64) * 16;  // wave-uniform LDS offset
-      const int pos = wbase + lane * 16;
+      const int pos = (i * C::THREADS + wave * 64 + lane) * 16;
       const int row = pos / C::ROW_BYTES;
       const int pch = (pos % C::ROW_BYTES) / 16;
-      int grow = j0 + row;
-      grow = grow < kend ? grow : kend - 1;
-      const size_t goffk = (size_t)grow * C::ROW_BYTES + (size_t)((pch ^ swz_k<C>(row)) * 16);
-      const size_t goffv = (size_t)grow * C::ROW_BYTES + (size_t)((pch ^ swz_v<C>(row)) * 16);
-      __builtin_amdgcn_global_load_lds((const void GLB_AS*)(Kg + goffk), (void LDS_AS*)(kl + wbase), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void GLB_AS*)(Vg + goffv), (void LDS_AS*)(vl + wbase), 16, 0, 0);
+      const int lch = pch ^ (is_v ? swz_v<C>(row) : swz_k<C>(row));
+      const int grow = row < last ? row : last;
+      const uint32_t o = (uint32_t)(grow * C::ROW_BYTES + lch * 16);
+      const uint32_t l = __builtin_amdgcn_readfirstlane(
+          lds_base + dst + (uint32_t)((i * C::THREADS + wave * 64) * 16));
+      dma16(gt, o, l);
     }
   };
-
-  if (ntiles > 0) issue_tile(0, 0);
+  const int wq0 = q0 + wave * 32 * QB;  // first query row of this wave
+  auto need_mask = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * BN;
+    return (j0 + BN > L) || (CAUSAL && (j0 + BN - 1 > wq0));
+  };
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane (h, c) holds
-  //      Q[q0 + 32*wave + c][16*ks + 8*h .. +7] for every ks ----
-  const int qrow = q0 + wave * 32 + col;
-  const int qrow_c = qrow < N ? qrow : N - 1;
-  bf16x8 qf[D / 16];
+  //      Q[row of block qb][16*ks + 8*h .. +7] for every ks ----
+  int qrow[QB];
+  bf16x8 qf[QB][D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qf[ks] = *(const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 16 + half * 8);
-
-  f32x16 acc[D / 32];
+  for (int qb = 0; qb < QB; ++qb) {
+    qrow[qb] = wq0 + qb * 32 + col;
+    const int qrow_c = qrow[qb] < N ? qrow[qb] : N - 1;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-
-  float m_run = -INFINITY;  // running shift, exp2 domain (scores * c)
-  float l_run = 0.f;        // this lane's partial row sum (its 16 keys of each 32)
-
-  // first query row of this wave: blocks entirely above the diagonal are skipped
-  const int wq0 = q0 + wave * 32;
-
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, stage ^ 1);
-
-    const char LDS_AS* kl = smem + stage * C::STAGE_BYTES;
-    const char LDS_AS* vl = kl + C::TILE_BYTES;
-    const int j0 = t * BN;
-
-    // ---------------- S^T = K Q^T ----------------
-    f32x16 s[BN / 32];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = kb * 32 + col;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int ch = (2 * ks + half) ^ swz_k<C>(row);
-        const bf16x8 a = *(const bf16x8 LDS_AS*)(kl + row * C::ROW_BYTES + ch * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
-    }
-
-    // ---------------- mask (diagonal / padding tiles only) ----------------
-    const bool need_mask = (j0 + BN > L) || (CAUSAL && (j0 + BN - 1 > wq0));
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-          bool ok = key < L;
-          if (CAUSAL) ok = ok && (key <= qrow);
-          s[kb][r] = ok ? s[kb][r] : (NEG_SCALE ? INFINITY : -INFINITY);
-        }
-    }
-
-    // ---------------- online softmax (exp2 domain) ----------------
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = NEG_SCALE ? fminf(mx, s[kb][r]) : fmaxf(mx, s[kb][r]);
-    {
-      const u32x2 pr = swap_halves(mx);
-      mx = NEG_SCALE ? fminf(__uint_as_float(pr[0]), __uint_as_float(pr[1]))
-                     : fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-    }
-    const float m_tile = mx * c;  // row maximum of scores * c (-inf if fully masked)
-    const bool grow = m_tile > m_run + kTauLog2;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    // P = exp2(S*c - m), rounded to bf16, packed as the B operand of O^T += V^T P^T
-    bf16x8 pb[BN / 16];
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        bf16x8 p;
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8)
-          p[t8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][sp * 8 + t8], c, -m_use));
-        pb[kb * 2 + sp] = p;
-      }
-    {
-      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-      for (int i = 0; i < BN / 16; ++i)
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
-          const bf16x2 pp = {pb[i][2 * t2], pb[i][2 * t2 + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-        }
-    }
-
-    // ---------------- O^T += V^T P^T ----------------
-    // transpose read: lane 16g + 4j + q supplies V row (16*step + 8u + 4h + j),
-    // columns 32db + 16(g%2) + 4q .. +3; lane 16g + i receives column
-    // 32db + 16(g%2) + i of those four rows.
-    const int g = lane / 16;
-    const int jr = (lane % 16) / 4;
-    const int qq = lane % 4;
-#pragma unroll
-    for (int st = 0; st < BN / 16; ++st) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        bf16x8 a;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int row = st * 16 + u * 8 + half * 4 + jr;
-          const int colb = (db * 32 + (g % 2) * 16 + qq * 4) * 2;  // byte offset in row
-          const int ch = (colb / 16) ^ swz_v<C>(row);
-          const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 LDS_AS*)(vl + row * C::ROW_BYTES + ch * 16 + (colb % 16)));
-          const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
-        }
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
-      }
-    }
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[qb][ks] = *(const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 16 + half * 8);
   }
+  // Q operands must have arrived before the key loop: an empty asm that reads
+  // them makes the compiler wait for their loads here, so that no wait for a
+  // load of its own lands inside the loop, where the only vector-memory
+  // operations are the tile DMAs (awaited explicitly before each barrier).
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[qb][ks]));
 
-  // ---------------- epilogue: O = O^T / l ----------------
-  const u32x2 lp = swap_halves(l_run);
-  const float l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
-    __bf16* orow = Os + (size_t)qrow * D;
+  f32x16 acc[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        bf16x4 o;
+      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
+
+  float m_run[QB], l_run[QB], alpha[QB];  // shift (exp2 domain), partial sum, pending rescale
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[db][a4 * 4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + a4 * 8 + half * 4) = o;
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+    alpha[qb] = 1.f;
+  }
+  bool resc = false;  // wave-uniform: a rescale is pending
+
+  // shift update after a new tile's scores: lazily, only when some row's
+  // maximum exceeds the current shift by more than 2^TAU
+  auto update_shift = [&](const f32x16 (&s)[QB][BN / 32]) __attribute__((always_inline)) {
+    float m_tile[QB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_tile[qb] = row_extreme<BN, NEG_SCALE>(s[qb]) * c;
+      grow = grow || (m_tile[qb] > m_run[qb] + kTauLog2);
+    }
+    resc = __builtin_amdgcn_ballot_w64(grow) != 0;
+    if (resc) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], m_tile[qb]);
+        alpha[qb] = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
       }
+    }
+  };
+  auto apply_rescale = [&]() __attribute__((always_inline)) {
+    if (resc) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha[qb];
+        l_run[qb] *= alpha[qb];
+      }
+      resc = false;
+    }
+  };
+  auto softmax_all = [&](const f32x16 (&s)[QB][BN / 32], bf16x8 (&pb)[QB][BN / 16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      softmax_p<BN>(s[qb], c, m_use, pb[qb], l_run[qb]);
+    }
+  };
+
+  f32x16 s0[QB][BN / 32], s1[QB][BN / 32];
+  bf16x8 pb[QB][BN / 16];
+
+  if (MODE == 0) {
+    constexpr int AHEAD = C::STAGES - 1;
+    auto sk = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t % C::STAGES) * C::STAGE_BYTES); };
+    auto sv = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t % C::STAGES) * C::STAGE_BYTES + C::TILE_BYTES); };
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i)
+      if (i < ntiles) {
+        issue(Kg, false, i, sk(i));
+        issue(Vg, true, i, sv(i));
+      }
+    wait_dma();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const bool more = t + AHEAD < ntiles;
+      if (more) {
+        issue(Kg, false, t + AHEAD, sk(t + AHEAD));
+        issue(Vg, true, t + AHEAD, sv(t + AHEAD));
+      }
+      if (ATTNIO_PRIO) __builtin_amdgcn_s_setprio(1);
+      if (ATTNIO_PF) qk_tile_pf<C, D, BN, QB>(smem + sk(t), qf, s0, col, half);
+      else qk_tile<C, D, BN, QB>(smem + sk(t), qf, s0, col, half);
+      if (ATTNIO_SEQ_HINT) seq_qk_hint<(D / 16) * (BN / 32), QB>();
+      if (ATTNIO_PRIO) __builtin_amdgcn_s_setprio(0);
+      if (need_mask(t)) mask_tile<BN, QB, CAUSAL, NEG_SCALE>(s0, t * BN, L, qrow, half);
+      update_shift(s0);
+      apply_rescale();
+      softmax_all(s0, pb);
+      if (ATTNIO_PRIO) __builtin_amdgcn_s_setprio(1);
+      if (ATTNIO_PF) pv_tile_pf<C, D, BN, QB>(smem + sv(t), pb, acc, lane, half);
+      else pv_tile<C, D, BN, QB>(smem + sv(t), pb, acc, lane, half);
+      if (ATTNIO_SEQ_HINT) seq_pv_hint<(BN / 16) * (D / 32), QB>();
+      if (ATTNIO_PRIO) __builtin_amdgcn_s_setprio(0);
+      // tile t + 1 must have landed; the DMAs of tiles t + 2 .. t + AHEAD may
+      // stay in flight (2 * LOADS instructions per tile and wave)
+      if (more) wait_dma_n<(AHEAD - 1) * 2 * C::LOADS>();
+      else wait_dma();
+      __syncthreads();
+    }
+  } else if (MODE == 2) {
+    // Ping-pong: the waves split into two groups of WAVES/2 (one wave of each
+    // group per SIMD).  Barriers stagger them by half a tile, so that on every
+    // SIMD one group runs its MFMA phase while the other runs its VALU phase:
+    //   slot 1: group 0 MFMA(t)   || group 1 VALU(t-1)
+    //   slot 2: group 0 VALU(t)   || group 1 MFMA(t)
+    // MFMA(t) = O += V(t-1)^T P(t-1)^T, then S(t) = K(t) Q^T;
+    // VALU(t) = mask, shift update, rescale, P(t) = exp2(S(t) c - m).
+    // K and V tiles have two LDS buffers each; the DMAs of K(t+1) and V(t)
+    // are issued at the start of slot 1 and awaited before the barrier that
+    // ends slot 2.
+#ifndef ATTNIO_PP_INTERLEAVED
+#define ATTNIO_PP_INTERLEAVED 0
+#endif
+    const int grp = ATTNIO_PP_INTERLEAVED ? wave % 2 : wave / (WAVES / 2);  // wave-uniform
+    auto kd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t & 1) * C::TILE_BYTES); };
+    auto vd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((2 + (t & 1)) * C::TILE_BYTES); };
+    auto mfma_phase = [&](int t) __attribute__((always_inline)) {
+      if (ATTNIO_PRIO) __builtin_amdgcn_s_setprio(2);
+      if (t >= 1) {
+        if (ATTNIO_PF) pv_tile_pf<C, D, BN, QB>(smem + vd(t - 1), pb, acc, lane, half);
+        else pv_tile<C, D, BN, QB>(smem + vd(t - 1), pb, acc, lane, half);
+        if (ATTNIO_SEQ_HINT) seq_pv_hint<(BN / 16) * (D / 32), QB>();
+      }
+      if (t < ntiles) {
+        if (ATTNIO_PF) qk_tile_pf<C, D, BN, QB>(smem + kd(t), qf, s0, col, half);
+        else qk_tile<C, D, BN, QB>(smem + kd(t), qf, s0, col, half);
+        if (ATTNIO_SEQ_HINT) seq_qk_hint<(D / 16) * (BN / 32), QB>();
+      }
+      if (ATTNIO_PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+    auto valu_phase = [&](int t) __attribute__((always_inline)) {
+      if (need_mask(t)) mask_tile<BN, QB, CAUSAL, NEG_SCALE>(s0, t * BN, L, qrow, half);
+      update_shift(s0);
+      apply_rescale();
+      softmax_all(s0, pb);
+    };
+    // Every wave runs the same straight loop MFMA(t), barrier, VALU(t),
+    // barrier; group 1 passes one extra barrier first, which shifts it half a
+    // tile behind group 0 (barriers count arrivals, not program locations).
+    // Global half-step h = 2t starts group 0's MFMA(t) and group 1's
+    // VALU(t-1): every wave issues its share of the DMAs of K(t+1), V(t) at
+    // its own h = 2t point and waits for them at the end of h = 2t+1.
+    auto issue_step = [&](int t) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) issue(Kg, false, t + 1, kd(t + 1));
+      if (t < ntiles) issue(Vg, true, t, vd(t));
+    };
+    if (ntiles > 0) {
+      issue(Kg, false, 0, kd(0));
+      wait_dma();
+      __syncthreads();
+      if (grp == 1) {
+        issue_step(0);
+        __syncthreads();
+      }
+      for (int t = 0; t < ntiles; ++t) {
+        if (grp == 0) issue_step(t);
+        mfma_phase(t);
+        if (grp == 1) wait_dma();
+        __syncthreads();
+        if (grp == 1) issue_step(t + 1);
+        valu_phase(t);
+        if (grp == 0) wait_dma();
+        __syncthreads();
+      }
+      mfma_phase(ntiles);  // O += V(last)^T P(last)^T
+      if (grp == 0) __syncthreads();
+    }
+  } else {
+    // K stages at 0 and TILE_BYTES, V stages at 2 and 3 TILE_BYTES
+    auto kd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t & 1) * C::TILE_BYTES); };
+    auto vd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((2 + (t & 1)) * C::TILE_BYTES); };
+    if (ntiles > 0) {
+      issue(Kg, false, 0, kd(0));
+      issue(Vg, true, 0, vd(0));
+      if (ntiles > 1) issue(Kg, false, 1, kd(1));
+    }
+    wait_dma();
+    __syncthreads();
+    if (ntiles > 0) {
+      qk_tile<C, D, BN, QB>(smem + kd(0), qf, s0, col, half);
+      if (need_mask(0)) mask_tile<BN, QB, CAUSAL, NEG_SCALE>(s0, 0, L, qrow, half);
+      update_shift(s0);
+    }
+    // every wave has finished reading K stage 0 before K(2) overwrites it
+    __syncthreads();
+
+    // steady-state step for a tile t that has a successor; sc holds S(t), sn
+    // receives S(t+1)
+    auto step = [&](f32x16 (&sc)[QB][BN / 32], f32x16 (&sn)[QB][BN / 32], int t) __attribute__((always_inline)) {
+      if (t + 2 < ntiles) issue(Kg, false, t + 2, kd(t + 2));
+      issue(Vg, true, t + 1, vd(t + 1));
+      apply_rescale();
+      // phase A: S(t+1) on MFMA while P(t) is formed on the VALU
+      qk_tile<C, D, BN, QB>(smem + kd(t + 1), qf, sn, col, half);
+      softmax_all(sc, pb);
+      interleave_hint<(D / 16) * (BN / 32) * QB, ATTNIO_HINT_VALU, QB, 2>();
+      // phase B: O += V(t)^T P(t)^T while S(t+1) is reduced
+      if (need_mask(t + 1)) mask_tile<BN, QB, CAUSAL, NEG_SCALE>(sn, (t + 1) * BN, L, qrow, half);
+      pv_tile<C, D, BN, QB>(smem + vd(t), pb, acc, lane, half);
+      update_shift(sn);
+      wait_dma();
+      __syncthreads();
+    };
+    // final tile: no successor to overlap with
+    auto last = [&](f32x16 (&sc)[QB][BN / 32], int t) __attribute__((always_inline)) {
+      apply_rescale();
+      softmax_all(sc, pb);
+      pv_tile<C, D, BN, QB>(smem + vd(t), pb, acc, lane, half);
+    };
+    // unrolled by two so that S(t) and S(t+1) alternate between s0 and s1
+    // without register copies
+    if (ntiles > 0) {
+      int t = 0;
+      for (;;) {
+        if (t + 1 >= ntiles) { last(s0, t); break; }
+        step(s0, s1, t);
+        ++t;
+        if (t + 1 >= ntiles) { last(s1, t); break; }
+        step(s1, s0, t);
+        ++t;
+      }
+    }
+  }
+
+  // ---------------- epilogue: O = O^T / l ----------------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const u32x2 lp = swap_halves(l_run[qb]);
+    const float l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow[qb] < N) {
+      __bf16* orow = Os + (size_t)qrow[qb] * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[qb][db][a4 * 4 + e] * inv);
+          *(bf16x4*)(orow + db * 32 + a4 * 8 + half * 4) = o;
+        }
+    }
   }
 }
 
-template <int D, int BN, int WAVES, bool CAUSAL, bool NEG>
+template <int D, int BN, int WAVES, int QB, int STAGES, int MODE, bool CAUSAL, bool NEG>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  using C = Cfg<D, BN, WAVES>;
+  using C = Cfg<D, BN, WAVES, QB, MODE == 0 ? STAGES : 2>;
   const int n_qtiles = (a.N + C::BM - 1) / C::BM;
   const long long grid = (long long)a.B * a.H * n_qtiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = a.scale * kLog2e;
-  auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, CAUSAL, NEG>;
+  auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, QB, STAGES, MODE, CAUSAL, NEG>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
                      a.kv_len, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
 }
 
-template <int D, int BN, int WAVES>
+template <class P>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t stream) {
+  constexpr int D = P::D, BN = P::BN, W = P::WAVES, QB = P::QB, ST = P::STAGES;
+  constexpr int OV = P::MODE;
   const bool neg = a.scale < 0.f;
-  if (a.causal) return neg ? launch_t<D, BN, WAVES, true, true>(a, stream)
-                           : launch_t<D, BN, WAVES, true, false>(a, stream);
-  return neg ? launch_t<D, BN, WAVES, false, true>(a, stream)
-             : launch_t<D, BN, WAVES, false, false>(a, stream);
+  if (a.causal) return neg ? launch_t<D, BN, W, QB, ST, OV, true, true>(a, stream)
+                           : launch_t<D, BN, W, QB, ST, OV, true, false>(a, stream);
+  return neg ? launch_t<D, BN, W, QB, ST, OV, false, true>(a, stream)
+             : launch_t<D, BN, W, QB, ST, OV, false, false>(a, stream);
+}
+
+// Tile shape per head size (see the I/O model in the C-ABI front end).
+#ifndef ATTNIO_BN_D128
+#define ATTNIO_BN_D128 128
+#endif
+#ifndef ATTNIO_BN_D64
+#define ATTNIO_BN_D64 64
+#endif
+#ifndef ATTNIO_QB_D128
+#define ATTNIO_QB_D128 1
+#endif
+#ifndef ATTNIO_QB_D64
+#define ATTNIO_QB_D64 1
+#endif
+#ifndef ATTNIO_STAGES_D128
+#define ATTNIO_STAGES_D128 2
+#endif
+#ifndef ATTNIO_STAGES_D64
+#define ATTNIO_STAGES_D64 2
+#endif
+// loop form: 0 sequential, 1 software-pipelined, 2 ping-pong wave groups
+#ifndef ATTNIO_MODE_D128
+#define ATTNIO_MODE_D128 2
+#endif
+#ifndef ATTNIO_MODE_D64
+#define ATTNIO_MODE_D64 2
+#endif
+#ifndef ATTNIO_WAVES_D128
+#define ATTNIO_WAVES_D128 8
+#endif
+#ifndef ATTNIO_WAVES_D64
+#define ATTNIO_WAVES_D64 8
+#endif
+template <int HD> struct Pick;
+template <> struct Pick<128> {
+  static constexpr int D = 128, BN = ATTNIO_BN_D128, WAVES = ATTNIO_WAVES_D128, QB = ATTNIO_QB_D128;
+  static constexpr int STAGES = ATTNIO_STAGES_D128;
+  static constexpr int MODE = ATTNIO_MODE_D128;
+};
+template <> struct Pick<64> {
+  static constexpr int D = 64, BN = ATTNIO_BN_D64, WAVES = ATTNIO_WAVES_D64, QB = ATTNIO_QB_D64;
+  static constexpr int STAGES = ATTNIO_STAGES_D64;
+  static constexpr int MODE = ATTNIO_MODE_D64;
+};
+
+template <class P>
+void fill_tiling(Tiling* t) {
+  using C = Cfg<P::D, P::BN, P::WAVES, P::QB, P::MODE == 0 ? P::STAGES : 2>;
+  *t = {C::BM, P::BN, C::STAGES, P::WAVES, C::LDS_BYTES};
 }
 
 }  // namespace
 
 bool bf16_tiling(int d, int causal, Tiling* t) {
   (void)causal;
-  if (d == 128) {
-    using C = Cfg<128, 64, 4>;
-    *t = {C::BM, 64, C::STAGES, 4, C::LDS_BYTES};
-    return true;
-  }
-  if (d == 64) {
-    using C = Cfg<64, 64, 4>;
-    *t = {C::BM, 64, C::STAGES, 4, C::LDS_BYTES};
-    return true;
-  }
+  if (d == 128) { fill_tiling<Pick<128>>(t); return true; }
+  if (d == 64) { fill_tiling<Pick<64>>(t); return true; }
   return false;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return dispatch_mask<128, 64, 4>(a, stream);
-  if (a.d == 64) return dispatch_mask<64, 64, 4>(a, stream);
+  if (a.d == 128) return dispatch_mask<Pick<128>>(a, stream);
+  if (a.d == 64) return dispatch_mask<Pick<64>>(a, stream);
   return hipErrorInvalidValue;
 }
 
