@@ -33,7 +33,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (no sparsity)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 DEFAULT_WORKLOAD = "bf16_causal_h32_n32k_d128"
 KERNEL_SOURCE = os.path.join(ROOT, "exact_long_sequence_amd", "csrc", "attn_fwd_bf16.hip")
-COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_h32_n32k_d128_counters.md")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_b1_h32_n32k_d128_counters.md")
 
 
 def kernel_source_digest() -> str:

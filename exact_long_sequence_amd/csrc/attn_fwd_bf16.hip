@@ -35,6 +35,7 @@
 // to rounding; probabilities are bounded by 2^TAU before normalisation.
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -727,7 +728,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + C::BM - 1) / C::BM;
   const long long grid = (long long)a.B * a.H * n_qtiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const float c = a.scale * kLog2e;
+  // exponent multiplier scale * log2(e); an exact zero (scale 0, or a scale so
+  // small that the product underflows) becomes the smallest normal float, so
+  // masked scores (-inf) still map to exp2(-inf) = 0 while every visible
+  // score maps to exp2(0) = 1 exactly: uniform weights, as for c = 0
+  float c = a.scale * kLog2e;
+  if (c == 0.f) c = FLT_MIN;
   auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, QB, STAGES, MODE, CAUSAL, NEG>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,

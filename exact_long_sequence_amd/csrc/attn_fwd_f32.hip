@@ -15,6 +15,7 @@
 //   "IO-Aware Algorithms", How it works, online softmax).
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -151,9 +152,13 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int n_qtiles = (a.N + kQ - 1) / kQ;
   const long long grid = (long long)a.B * a.H * n_qtiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  // exponent multiplier scale * log2(e); an exact zero becomes the smallest
+  // normal float so that (-inf) * c stays -inf (uniform weights, no NaN)
+  float c = a.scale * kLog2e;
+  if (c == 0.f) c = FLT_MIN;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(256), 0,
                      stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
-                     a.kv_len, a.H, a.N, a.scale * kLog2e, n_qtiles);
+                     a.kv_len, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
 }
 
