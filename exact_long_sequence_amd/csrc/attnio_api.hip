@@ -144,13 +144,9 @@ int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
   const double row = (double)d * elem_bytes;
   const long long BM = t.BM, BN = t.BN;
   const long long nqt = (N + BM - 1) / BM;
-  // query tiles of one head resident together on one XCD (32 CUs); the
-  // workgroups per CU follow from the LDS budget of 160 KiB and two waves
-  // per SIMD.
-  const long long wg_per_cu_lds = (160 * 1024) / (t.lds_bytes > 0 ? t.lds_bytes : 1);
-  const long long wg_per_cu_waves = (4 * (d == 64 ? 4 : 2)) / t.waves;
-  const long long wg_per_cu = wg_per_cu_lds < wg_per_cu_waves ? wg_per_cu_lds : wg_per_cu_waves;
-  const long long resident = 32 * (wg_per_cu > 0 ? wg_per_cu : 1);
+  // query tiles of one head run together on one XCD (32 CUs), `resident` at
+  // a time; each such generation streams the keys it needs through L2 once
+  const long long resident = 32LL * (t.wg_per_cu > 0 ? t.wg_per_cu : 1);
   double t_min = 4.0 * B, t_lds = 0, t_l2 = 0, pairs = 0;
   for (int b = 0; b < B; ++b) {
     long long L = N;
@@ -170,7 +166,9 @@ int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
         t_lds += row * (double)BM + 2.0 * row * (double)(tiles * BN);
       }
       // one generation = `resident` query tiles running together; K/V of the
-      // keys that generation needs come from HBM once per generation
+      // keys that generation needs come from beyond L2 once per generation
+      // (a lower bound for this schedule: it assumes the generation's
+      // workgroups walk the keys in step)
       for (long long g0 = 0; g0 < nqt; g0 += resident) {
         // causal tiles run longest first: generation g covers the highest
         // remaining query tiles, so it needs keys up to its first tile's end

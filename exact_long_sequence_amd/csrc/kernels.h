@@ -26,6 +26,7 @@ struct Tiling {
   int stages;  // K/V LDS buffers
   int waves;   // wavefronts per workgroup (32 query rows each)
   int lds_bytes;
+  int wg_per_cu;  // workgroups resident per CU (register and LDS bound)
 };
 
 bool bf16_tiling(int d, int causal, Tiling* t);
