@@ -28,27 +28,31 @@
 // An I/O Analysis for Long-Sequence Attention" (abstract, optimisation 3)
 // mapped onto 64-wide wavefronts.
 //
-// The rescale of the running output is lazy: the running maximum m only moves
-// when some row's maximum exceeds it by more than 2^TAU_LOG2 in the exp2
-// domain.  Any shift m >= the true maximum - TAU gives the same softmax (the
-// shift cancels between numerator and denominator), so the result is exact up
-// to rounding; probabilities are bounded by 2^TAU before normalisation.
+// The shift of the exponentials is lazy.  Any shift at or below the row
+// maximum gives the same softmax (it cancels between numerator and
+// denominator), so the shift is taken from the first key tile's row maxima
+// and moved again only when a tile's row sum shows that some probability
+// would exceed 2^16 (then to the current maxima, rescaling the running output
+// and row sum).  The result is exact up to rounding, every probability stays
+// in [0, 2^16], and the per-tile row maximum is not needed on the common path.
 //
 // Two loop forms share the per-tile building blocks (selected per head size
 // at the bottom of this file):
 //  * ping-pong (default): eight waves in two groups of four, one wave of each
 //    group per SIMD; barriers offset the groups by half a tile, so on every
-//    SIMD one group issues its MFMA chain while the other runs the softmax;
+//    SIMD one group issues its MFMA stream while the other runs the softmax;
 //  * sequential: four waves, each running S, softmax, O per tile in turn over
 //    an N-stage LDS ring; the overlap of MFMA with VALU then comes only from
 //    the other workgroup's waves on the same SIMD.
 // Both realise the three-level overlap of the I/O analysis (optimisation 2):
-// HBM/L2 -> LDS by DMA of later tiles, LDS -> VGPR operand reads under the
-// MFMA chains, and MFMA under the VALU softmax.
+// HBM/L2 -> LDS by DMA of later tiles, LDS -> VGPR operand reads ahead of the
+// MFMAs that use them, and MFMA under the VALU softmax.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -65,7 +69,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTauLog2 = 8.0f;  // lazy-rescale threshold (probabilities <= 2^8)
+constexpr float kTauLog2 = 8.0f;        // shift moves when a row maximum exceeds it by 2^8
+constexpr float kLazySumMax = 65536.f;  // a tile row sum above this recomputes the shift
 
 template <int D, int BN, int WAVES, int NSTAGES>
 struct Cfg {
@@ -132,23 +137,82 @@ __device__ __forceinline__ void wait_dma_n() {
 // them freely.
 // ----------------------------------------------------------------------------
 
-// S^T (BN keys x 32 queries) = K_tile Q^T: BN/32 independent accumulation chains
-template <class C, int D, int BN>
-__device__ __forceinline__ void qk_tile(const char LDS_AS* kl, const bf16x8 (&qf)[D / 16],
-                                        f32x16 (&s)[BN / 32], int col, int half) {
+// LDS operands are read this many MFMAs ahead of their use.  One wave per SIMD
+// issues the whole MFMA chain of a phase, so the LDS latency must be covered by
+// its own earlier MFMAs; measured on MI355X, a distance of 2 or more keeps a
+// lone 32x32x16 chain at its full rate of one MFMA per 32 cycles even with
+// 1 KiB of LDS reads per MFMA, while reading 1-2 ahead (what the compiler
+// schedules on its own) costs about 40%.
+constexpr int kReadAhead = 4;
+
+// One MFMA phase as a single stream of MFMAs:
+//   DO_PV: O^T (D x 32 queries) += V_tile^T P^T   ((BN/16) x (D/32) MFMAs)
+//   DO_QK: S^T (BN keys x 32 queries) = K_tile Q^T ((D/16) x (BN/32) MFMAs)
+// in that order.  Each group of D/32 (resp. BN/32) consecutive MFMAs writes
+// independent accumulators, so dependent MFMAs are at least 4 apart.
+//
+// The V operand uses the transpose read: lane 16g + 4j + q supplies V row
+// (16 st + 8u + 4h + j), columns 32 db + 16 (g % 2) + 4 q .. +3, and lane
+// 16g + i receives column 32 db + 16 (g % 2) + i of those four rows, which is
+// the A-operand layout (d down the rows, keys along k).  The key order inside
+// each 16-key step matches the order in which the S^T accumulator holds the
+// same keys, so P needs no register shuffle.  The K operand is one 16-byte
+// read of row kb*32 + c.  A scheduling barrier after every MFMA pins the
+// read-ahead distance.
+template <class C, int D, int BN, bool DO_PV, bool DO_QK>
+__device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 (&pb)[BN / 16],
+                                            f32x16 (&acc)[D / 32], const char LDS_AS* kl,
+                                            const bf16x8 (&qf)[D / 16], f32x16 (&s)[BN / 32],
+                                            int lane) {
+  const int half = lane / 32, col = lane % 32;
+  const int g = lane / 16;
+  const int jr = (lane % 16) / 4;
+  const int qq = lane % 4;
+  constexpr int NPV = DO_PV ? (BN / 16) * (D / 32) : 0;
+  constexpr int NQK = DO_QK ? (D / 16) * (BN / 32) : 0;
+  constexpr int NM = NPV + NQK;
+  constexpr int R = kReadAhead;
+  auto read = [&](int m) __attribute__((always_inline)) {
+    bf16x8 a;
+    if (m < NPV) {
+      const int st = m / (D / 32), db = m % (D / 32);
 #pragma unroll
-  for (int kb = 0; kb < BN / 32; ++kb)
+      for (int u = 0; u < 2; ++u) {
+        const int row = st * 16 + u * 8 + half * 4 + jr;
+        const int colb = (db * 32 + (g % 2) * 16 + qq * 4) * 2;  // byte offset in the row
+        const int ch = (colb / 16) ^ swz_v<C>(row);
+        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4 LDS_AS*)(vl + row * C::ROW_BYTES + ch * 16 + (colb % 16)));
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+        for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
+      }
+    } else {
+      const int mq = m - NPV;
+      const int ks = mq / (BN / 32), kb = mq % (BN / 32);
       const int row = kb * 32 + col;
       const int ch = (2 * ks + half) ^ swz_k<C>(row);
-      const bf16x8 a = *(const bf16x8 LDS_AS*)(kl + row * C::ROW_BYTES + ch * 16);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      a = *(const bf16x8 LDS_AS*)(kl + row * C::ROW_BYTES + ch * 16);
     }
+    return a;
+  };
+  bf16x8 ring[R + 1];
+#pragma unroll
+  for (int m = 0; m < R && m < NM; ++m) ring[m] = read(m);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m + R < NM) ring[(m + R) % (R + 1)] = read(m + R);
+    const bf16x8 a = ring[m % (R + 1)];
+    if (m < NPV) {
+      const int st = m / (D / 32), db = m % (D / 32);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
+    } else {
+      const int mq = m - NPV;
+      const int ks = mq / (BN / 32), kb = mq % (BN / 32);
+      const f32x16 zero = {};
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -168,26 +232,33 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[BN / 32], int j0, int L, i
 }
 
 // Row extreme of the raw scores (max, or min for a negative scale), over the
-// lane's 16 values per block and the partner lane 32 apart.
+// lane's 16 values per block and the partner lane 32 apart.  Four independent
+// chains: a single chain of dependent max operations is bound by VALU latency.
 template <int BN, bool NEG>
 __device__ __forceinline__ float row_extreme(const f32x16 (&s)[BN / 32]) {
-  float mx = s[0][0];
+  float m4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) m4[k] = s[0][k];
 #pragma unroll
   for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = NEG ? fminf(mx, s[kb][r]) : fmaxf(mx, s[kb][r]);
+    for (int r = (kb == 0 ? 4 : 0); r < 16; ++r)
+      m4[r % 4] = NEG ? fminf(m4[r % 4], s[kb][r]) : fmaxf(m4[r % 4], s[kb][r]);
+  const float mx = NEG ? fminf(fminf(m4[0], m4[1]), fminf(m4[2], m4[3]))
+                       : fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
   const u32x2 pr = swap_halves(mx);
   return NEG ? fminf(__uint_as_float(pr[0]), __uint_as_float(pr[1]))
              : fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
 }
 
 // P = exp2(S*c - m) rounded to bf16 and packed as the B operands of the P x V
-// MFMA (operand i covers keys 16 i .. 16 i + 15 of the tile); the lane's
-// partial row sum accumulates the rounded values.
+// MFMA (operand i covers keys 16 i .. 16 i + 15 of the tile).  Returns this
+// lane's sum of the rounded values over the tile (four independent chains).
 template <int BN>
-__device__ __forceinline__ void softmax_p(const f32x16 (&s)[BN / 32], float c, float m_use,
-                                          bf16x8 (&pb)[BN / 16], float& l_run) {
+__device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, float m_use,
+                                           bf16x8 (&pb)[BN / 16]) {
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -199,43 +270,11 @@ __device__ __forceinline__ void softmax_p(const f32x16 (&s)[BN / 32], float c, f
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2) {
         const bf16x2 pp = {p[2 * t2], p[2 * t2 + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+        l4[t2] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l4[t2], false);
       }
       pb[kb * 2 + sp] = p;
     }
-}
-
-// O^T (D x 32 queries) += V_tile^T P^T.  The transpose read: lane 16g + 4j + q
-// supplies V row (16 st + 8u + 4h + j), columns 32 db + 16 (g % 2) + 4 q .. +3,
-// and lane 16g + i receives column 32 db + 16 (g % 2) + i of those four rows,
-// which is the A-operand layout (d down the rows, keys along k).  The key order
-// inside each 16-key step matches the order in which the S^T accumulator holds
-// the same keys, so no register shuffle is needed.
-template <class C, int D, int BN>
-__device__ __forceinline__ void pv_tile(const char LDS_AS* vl, const bf16x8 (&pb)[BN / 16],
-                                        f32x16 (&acc)[D / 32], int lane, int half) {
-  const int g = lane / 16;
-  const int jr = (lane % 16) / 4;
-  const int qq = lane % 4;
-#pragma unroll
-  for (int st = 0; st < BN / 16; ++st) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      bf16x8 a;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = st * 16 + u * 8 + half * 4 + jr;
-        const int colb = (db * 32 + (g % 2) * 16 + qq * 4) * 2;  // byte offset in the row
-        const int ch = (colb / 16) ^ swz_v<C>(row);
-        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 LDS_AS*)(vl + row * C::ROW_BYTES + ch * 16 + (colb % 16)));
-        const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
-      }
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
-    }
-  }
+  return (l4[0] + l4[1]) + (l4[2] + l4[3]);
 }
 
 // ----------------------------------------------------------------------------
@@ -299,26 +338,32 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   __bf16* Os = O + slice;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
-  // DMA of K or V tile t into LDS byte offset `dst` of the ring.  Load i of a
-  // lane fills LDS bytes pos = (i*THREADS + 64*wave + lane)*16 of the tile,
-  // i.e. row pos / ROW_BYTES and physical chunk (pos % ROW_BYTES) / 16; the
-  // lane fetches the logical chunk that the swizzle stores there.  A tail tile
-  // clamps rows >= kend to kend - 1 (masked keys: they only need to be finite
-  // memory inside the tensor; keys >= kv_len are never read).
-  auto issue = [&](const char* gsrc, bool is_v, int t, uint32_t dst) __attribute__((always_inline)) {
+  // DMA of K or V tile t into LDS byte offset `dst` of the ring, by NW waves
+  // starting at wave W0 (each issues TILE_BYTES / (1 KiB * NW) loads).  Load i
+  // of a lane fills LDS bytes pos = (i*64*NW + 64*(wave-W0) + lane)*16 of the
+  // tile, i.e. row pos / ROW_BYTES and physical chunk (pos % ROW_BYTES) / 16;
+  // the lane fetches the logical chunk that the swizzle stores there.  A tail
+  // tile clamps rows >= kend to kend - 1 (masked keys: they only need to be
+  // finite memory inside the tensor; keys >= kv_len are never read).
+  auto issue = [&](auto nw_tag, int w0, const char* gsrc, bool is_v, int t, uint32_t dst)
+      __attribute__((always_inline)) {
+    constexpr int NW = decltype(nw_tag)::value;
+    constexpr int TH = 64 * NW;
+    constexpr int NLOADS = C::TILE_BYTES / 16 / TH;
+    static_assert(C::TILE_BYTES % (16 * TH) == 0, "tile must split evenly over the issuing waves");
     const int j0 = t * BN;
     const char* gt = gsrc + (size_t)j0 * C::ROW_BYTES;
     const int last = kend - 1 - j0;  // last valid row of this tile
+    const int wl = wave - w0;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int pos = (i * C::THREADS + wave * 64 + lane) * 16;
+    for (int i = 0; i < NLOADS; ++i) {
+      const int pos = (i * TH + wl * 64 + lane) * 16;
       const int row = pos / C::ROW_BYTES;
       const int pch = (pos % C::ROW_BYTES) / 16;
       const int lch = pch ^ (is_v ? swz_v<C>(row) : swz_k<C>(row));
       const int grow = row < last ? row : last;
       const uint32_t o = (uint32_t)(grow * C::ROW_BYTES + lch * 16);
-      const uint32_t l = __builtin_amdgcn_readfirstlane(
-          lds_base + dst + (uint32_t)((i * C::THREADS + wave * 64) * 16));
+      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_base + dst + (uint32_t)((i * TH + wl * 64) * 16));
       dma16(gt, o, l);
     }
   };
@@ -352,39 +397,39 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
   float m_run = -INFINITY;  // running shift, exp2 domain (scores * c)
   float l_run = 0.f;        // this lane's partial row sum (its 16 keys of each 32)
-  float alpha = 1.f;        // pending rescale of acc and l
-  bool resc = false;        // wave-uniform: a rescale is pending
 
   f32x16 s0[BN / 32];
   bf16x8 pb[BN / 16];
 
-  // shift update after a new tile's scores: lazily, only when some row's
-  // maximum exceeds the current shift by more than 2^TAU
+  // Move the shift to the current row extremes of s0 where some row's extreme
+  // exceeds it by more than 2^TAU, rescaling acc and l (wave-uniform branch).
   auto update_shift = [&]() __attribute__((always_inline)) {
     const float m_tile = row_extreme<BN, NEG_SCALE>(s0) * c;
-    resc = __builtin_amdgcn_ballot_w64(m_tile > m_run + kTauLog2) != 0;
-    if (resc) {
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTauLog2) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
-      alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-    }
-  };
-  auto apply_rescale = [&]() __attribute__((always_inline)) {
-    if (resc) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       l_run *= alpha;
-      resc = false;
     }
   };
-  // VALU part of tile t: mask, shift update, rescale, P(t)
+  // VALU part of tile t: mask, P(t), row sums.  The shift is computed on the
+  // first tile and afterwards only when this tile's row sum shows that some
+  // probability would exceed 2^16 (or is not finite); any shift at or below
+  // the row maximum gives the same softmax, so the result is exact up to
+  // rounding and every probability stays within [0, 2^16].
   auto softmax_tile = [&](int t) __attribute__((always_inline)) {
     if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0, t * BN, L, qrow, half);
-    update_shift();
-    apply_rescale();
-    softmax_p<BN>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb, l_run);
+    if (t == 0) update_shift();
+    float lt = softmax_p<BN>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+    if (t > 0 && __builtin_amdgcn_ballot_w64(!(lt <= kLazySumMax)) != 0) {
+      update_shift();
+      lt = softmax_p<BN>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+    }
+    l_run += lt;
   };
 
   if (PINGPONG) {
@@ -395,72 +440,85 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     //   VALU(t) = softmax of tile t;
     // group 1 passes one extra barrier first, which shifts it half a tile
     // behind group 0 (a barrier counts arrivals, not program locations), so on
-    // each SIMD one group's MFMA chain runs under the other's softmax.  The
+    // each SIMD one group's MFMA stream runs under the other's softmax.  The
     // MFMA phase runs at raised wave priority.  K and V tiles have two LDS
     // buffers each.  Global half-step h = 2t starts group 0's MFMA(t) and
-    // group 1's VALU(t-1): every wave issues its share of the DMAs of K(t+1)
-    // and V(t) at its own h = 2t point and waits for them at the end of
-    // h = 2t + 1, before the barrier that publishes them.
+    // group 1's VALU(t-1); there group 1 issues the DMAs of K(t+1) and V(t)
+    // (its softmax has slack, group 0's MFMA stream has none) and waits for
+    // them at the end of h = 2t + 1, before the barrier that publishes them.
     const int grp = wave / (WAVES / 2);  // wave-uniform
     auto kd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t & 1) * C::TILE_BYTES); };
     auto vd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((2 + (t & 1)) * C::TILE_BYTES); };
-    auto mfma_phase = [&](int t) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_setprio(2);
-      if (t >= 1) pv_tile<C, D, BN>(smem + vd(t - 1), pb, acc, lane, half);
-      if (t < ntiles) qk_tile<C, D, BN>(smem + kd(t), qf, s0, col, half);
-      __builtin_amdgcn_s_setprio(0);
-    };
+    std::integral_constant<int, WAVES / 2> g1_tag;
+    std::integral_constant<int, WAVES> all_tag;
     auto issue_step = [&](int t) __attribute__((always_inline)) {
-      if (t + 1 < ntiles) issue(Kg, false, t + 1, kd(t + 1));
-      if (t < ntiles) issue(Vg, true, t, vd(t));
+      if (t + 1 < ntiles) issue(g1_tag, WAVES / 2, Kg, false, t + 1, kd(t + 1));
+      if (t < ntiles) issue(g1_tag, WAVES / 2, Vg, true, t, vd(t));
+    };
+    // one half-step pair of tile t; `mf` is the MFMA phase
+    auto step = [&](int t, auto&& mf) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(2);
+      mf();
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 1) wait_dma();
+      __syncthreads();
+      if (grp == 1) issue_step(t + 1);
+      softmax_tile(t);
+      // keep the softmax in this half step: without these uses the compiler
+      // sinks the exponentials past the barrier, next to the P x V MFMAs
+#pragma unroll
+      for (int i = 0; i < BN / 16; ++i) asm volatile("" ::"v"(pb[i]));
+      asm volatile("" ::"v"(l_run));
+      __syncthreads();
     };
     if (ntiles > 0) {
-      issue(Kg, false, 0, kd(0));
+      issue(all_tag, 0, Kg, false, 0, kd(0));
       wait_dma();
       __syncthreads();
       if (grp == 1) {
         issue_step(0);
         __syncthreads();
       }
-      for (int t = 0; t < ntiles; ++t) {
-        if (grp == 0) issue_step(t);
-        mfma_phase(t);
-        if (grp == 1) wait_dma();
-        __syncthreads();
-        if (grp == 1) issue_step(t + 1);
-        softmax_tile(t);
-        if (grp == 0) wait_dma();
-        __syncthreads();
-      }
-      mfma_phase(ntiles);  // O += V(last)^T P(last)^T
-      if (grp == 0) __syncthreads();
+      step(0, [&]() __attribute__((always_inline)) {
+        mfma_stream<C, D, BN, false, true>(smem, pb, acc, smem + kd(0), qf, s0, lane);
+      });
+      for (int t = 1; t < ntiles; ++t)
+        step(t, [&]() __attribute__((always_inline)) {
+          mfma_stream<C, D, BN, true, true>(smem + vd(t - 1), pb, acc, smem + kd(t), qf, s0, lane);
+        });
+      __builtin_amdgcn_s_setprio(2);
+      mfma_stream<C, D, BN, true, false>(smem + vd(ntiles - 1), pb, acc, smem, qf, s0, lane);
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 0) __syncthreads();  // group 1's last VALU barrier
     }
   } else {
     // Sequential form over an LDS ring of STAGES (K, V) tile pairs: the DMAs of
     // tile t + STAGES - 1 are in flight while tile t is computed.
     constexpr int AHEAD = C::STAGES - 1;
+    constexpr int LOADS = C::TILE_BYTES / 16 / C::THREADS;
+    std::integral_constant<int, WAVES> all_tag;
     auto sk = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t % C::STAGES) * C::STAGE_BYTES); };
     auto sv = [&](int t) __attribute__((always_inline)) { return sk(t) + (uint32_t)C::TILE_BYTES; };
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i)
       if (i < ntiles) {
-        issue(Kg, false, i, sk(i));
-        issue(Vg, true, i, sv(i));
+        issue(all_tag, 0, Kg, false, i, sk(i));
+        issue(all_tag, 0, Vg, true, i, sv(i));
       }
     wait_dma();
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const bool more = t + AHEAD < ntiles;
       if (more) {
-        issue(Kg, false, t + AHEAD, sk(t + AHEAD));
-        issue(Vg, true, t + AHEAD, sv(t + AHEAD));
+        issue(all_tag, 0, Kg, false, t + AHEAD, sk(t + AHEAD));
+        issue(all_tag, 0, Vg, true, t + AHEAD, sv(t + AHEAD));
       }
-      qk_tile<C, D, BN>(smem + sk(t), qf, s0, col, half);
+      mfma_stream<C, D, BN, false, true>(smem, pb, acc, smem + sk(t), qf, s0, lane);
       softmax_tile(t);
-      pv_tile<C, D, BN>(smem + sv(t), pb, acc, lane, half);
+      mfma_stream<C, D, BN, true, false>(smem + sv(t), pb, acc, smem, qf, s0, lane);
       // tile t + 1 must have landed; the DMAs of tiles t + 2 .. t + AHEAD may
       // stay in flight (2 * LOADS instructions per tile and wave)
-      if (more) wait_dma_n<(AHEAD - 1) * 2 * C::LOADS>();
+      if (more) wait_dma_n<(AHEAD - 1) * 2 * LOADS>();
       else wait_dma();
       __syncthreads();
     }
