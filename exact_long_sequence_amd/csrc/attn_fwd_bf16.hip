@@ -280,7 +280,8 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // ----------------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------------
-template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, bool KEYS_DOWN, bool CAUSAL, bool NEG_SCALE>
+template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WG_PER_CU, bool KEYS_SNAKE, bool CAUSAL,
+          bool NEG_SCALE>
 __global__ __launch_bounds__(64 * WAVES, 2)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -330,14 +331,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   int kend = L;
   if (CAUSAL) kend = min(kend, min(N, q0 + C::BM));
   const int ntiles = (kend + BN - 1) / BN;
-  // With KEYS_DOWN, causal workgroups walk their key tiles from the diagonal
-  // down to key 0.  Query tiles of one head that run together then touch each
-  // key tile within a short time window even when their speeds drift apart,
-  // so the tile is still in L2 for the later ones (ascending order loses that
-  // reuse once the first, shortest tile of a resident group finishes and its
-  // successor starts again from key 0).  Online softmax does not depend on the
-  // key order.
-  auto ktile = [&](int t) __attribute__((always_inline)) { return (CAUSAL && KEYS_DOWN) ? ntiles - 1 - t : t; };
+  // Key order (online softmax does not depend on it).  Causal query tiles of
+  // a head run on one XCD longest first, RESIDENT at a time; call each such
+  // group a generation.  With KEYS_SNAKE, even generations walk their keys up
+  // from key 0 and odd ones down from the diagonal, so each generation starts
+  // on the keys the previous one ended on, which are still in L2; otherwise
+  // all walk up.
+  constexpr int RESIDENT = 32 * WG_PER_CU;  // workgroups resident on one XCD
+  const bool keys_down = CAUSAL && KEYS_SNAKE && (((n_qtiles - 1 - qt) / RESIDENT) & 1);
+  auto ktile = [&](int t) __attribute__((always_inline)) { return keys_down ? ntiles - 1 - t : t; };
 
   const size_t slice = (size_t)bh * N * D;
   const __bf16* Qs = Q + slice;
@@ -552,7 +554,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   }
 }
 
-template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, bool KEYS_DOWN, bool CAUSAL, bool NEG>
+template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WPC, bool SNAKE, bool CAUSAL, bool NEG>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   using C = Cfg<D, BN, WAVES, PINGPONG ? 2 : STAGES>;
   const int n_qtiles = (a.N + C::BM - 1) / C::BM;
@@ -564,7 +566,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   // score maps to exp2(0) = 1 exactly: uniform weights, as for c = 0
   float c = a.scale * kLog2e;
   if (c == 0.f) c = FLT_MIN;
-  auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, STAGES, PINGPONG, KEYS_DOWN, CAUSAL, NEG>;
+  auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, STAGES, PINGPONG, WPC, SNAKE, CAUSAL, NEG>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
                      a.kv_len, a.H, a.N, c, n_qtiles);
@@ -573,13 +575,13 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 
 template <class P>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t stream) {
-  constexpr int D = P::D, BN = P::BN, W = P::WAVES, ST = P::STAGES;
-  constexpr bool PP = P::PINGPONG, KD = P::KEYS_DOWN;
+  constexpr int D = P::D, BN = P::BN, W = P::WAVES, ST = P::STAGES, WPC = P::WG_PER_CU;
+  constexpr bool PP = P::PINGPONG, SN = P::KEYS_SNAKE;
   const bool neg = a.scale < 0.f;
-  if (a.causal) return neg ? launch_t<D, BN, W, ST, PP, KD, true, true>(a, stream)
-                           : launch_t<D, BN, W, ST, PP, KD, true, false>(a, stream);
-  return neg ? launch_t<D, BN, W, ST, PP, KD, false, true>(a, stream)
-             : launch_t<D, BN, W, ST, PP, KD, false, false>(a, stream);
+  if (a.causal) return neg ? launch_t<D, BN, W, ST, PP, WPC, SN, true, true>(a, stream)
+                           : launch_t<D, BN, W, ST, PP, WPC, SN, true, false>(a, stream);
+  return neg ? launch_t<D, BN, W, ST, PP, WPC, SN, false, true>(a, stream)
+             : launch_t<D, BN, W, ST, PP, WPC, SN, false, false>(a, stream);
 }
 
 // Tile shape and loop form per head size.  Measured on MI355X (causal,
@@ -603,23 +605,27 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t stream) {
 // follows from the compiled register counts (d = 128: 249 VGPRs, 2 waves per
 // SIMD, so one 8-wave workgroup per CU, which also fills 128 KiB of LDS;
 // d = 64: 127 VGPRs, 4 waves per SIMD, two workgroups of 32 KiB LDS each).
-// KEYS_DOWN (causal key tiles from the diagonal down), measured on MI355X:
-// d = 128, N = 32768: bytes read beyond L2 2.61e9 -> 1.62e9 at equal speed;
-// d = 64, N = 131072: 3.26e9 -> 4.27e9, so that shape keeps ascending order.
+// KEYS_SNAKE: causal generations alternate the key direction (see the kernel).
+#ifndef ATTNIO_SNAKE_D128
+#define ATTNIO_SNAKE_D128 1
+#endif
+#ifndef ATTNIO_SNAKE_D64
+#define ATTNIO_SNAKE_D64 1
+#endif
 template <int HD> struct Pick;
 template <> struct Pick<128> {
   static constexpr int D = 128, BN = ATTNIO_BN_D128, WAVES = ATTNIO_PINGPONG ? 8 : 4;
   static constexpr int STAGES = ATTNIO_STAGES;
   static constexpr bool PINGPONG = ATTNIO_PINGPONG != 0;
   static constexpr int WG_PER_CU = ATTNIO_PINGPONG ? 1 : 2;
-  static constexpr bool KEYS_DOWN = true;
+  static constexpr bool KEYS_SNAKE = ATTNIO_SNAKE_D128 != 0;
 };
 template <> struct Pick<64> {
   static constexpr int D = 64, BN = ATTNIO_BN_D64, WAVES = ATTNIO_PINGPONG ? 8 : 4;
   static constexpr int STAGES = ATTNIO_STAGES;
   static constexpr bool PINGPONG = ATTNIO_PINGPONG != 0;
   static constexpr int WG_PER_CU = ATTNIO_PINGPONG ? 2 : 4;
-  static constexpr bool KEYS_DOWN = false;
+  static constexpr bool KEYS_SNAKE = ATTNIO_SNAKE_D64 != 0;
 };
 
 template <class P>

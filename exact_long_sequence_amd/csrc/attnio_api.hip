@@ -166,16 +166,21 @@ int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
         t_lds += row * (double)BM + 2.0 * row * (double)(tiles * BN);
       }
       // one generation = `resident` query tiles running together; K/V of the
-      // keys that generation needs come from beyond L2 once per generation
-      // (a lower bound for this schedule: it assumes the generation's
-      // workgroups walk the keys in step)
+      // keys that generation needs come from beyond L2 once per generation,
+      // assuming its workgroups walk the keys in step.  Causal generations
+      // alternate the key direction, so each one after the first starts on
+      // keys the previous one ended on: up to one L2 (4 MiB per XCD) of them
+      // is reused.
+      const double l2_keys = 4.0 * 1024.0 * 1024.0 / (2.0 * row);
       for (long long g0 = 0; g0 < nqt; g0 += resident) {
         // causal tiles run longest first: generation g covers the highest
         // remaining query tiles, so it needs keys up to its first tile's end
         const long long top = causal ? nqt - g0 : nqt;
         long long kend = L;
         if (causal) kend = kend < top * BM ? kend : (top * BM < N ? top * BM : N);
-        t_l2 += 2.0 * row * (double)kend;
+        double keys = (double)kend;
+        if (causal && g0 > 0) keys -= (l2_keys < keys ? l2_keys : keys);
+        t_l2 += 2.0 * row * keys;
       }
     }
   }

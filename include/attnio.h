@@ -94,9 +94,11 @@ int attn_query_tiling(int d, int causal, int* BM, int* BN, int* stages, int* wav
  *                  tile visits) -- the L2->LDS traffic of the tall-skinny
  *                  products, which shrinks as 1/BM;
  *   out[2] t_l2    predicted traffic beyond L2: the query tiles of one head
- *                  run on one XCD, as many at a time as fit its 32 CUs, and
- *                  each such group reads the K/V rows it needs once (a lower
- *                  bound; the kernels' own schedule decides the real figure);
+ *                  run on one XCD, as many at a time as fit its 32 CUs; each
+ *                  such group reads the K/V rows it needs once, and a causal
+ *                  group reuses up to one 4 MiB L2 of the keys the previous
+ *                  group ended on (groups alternate the key direction).  An
+ *                  idealised figure: it assumes a group walks its keys in step;
  *   out[3] flops   algorithmic FLOPs, 4*d per (query, visible key) pair;
  *   out[4] pairs   number of (query, visible key) pairs (one exp each).
  * Returns 0, or a negative code for invalid shapes. */

@@ -109,3 +109,25 @@ def test_io_model_closed_forms():
     assert m["t_lds"] == H * nqt * (t["BM"] * d * 2 + 2 * ntile * t["BN"] * d * 2)
     with pytest.raises(RuntimeError):
         attnio.attn_io_model(1, 1, 10, 72, 2, False)
+
+
+def test_io_model_l2_generations():
+    """Causal 32 heads x 32768 x 128: 8192 resident rows per XCD give four
+    generations needing 32K, 24K, 16K and 8K keys; each later one reuses 8192
+    keys (4 MiB of K+V rows of 512 B) from the previous, so K/V are read for
+    32K + 16K + 8K + 0 keys per head, and Q and O once: 1.375 x T_min."""
+    H, N, d = 32, 32768, 128
+    t = attnio.attn_query_tiling(d, True)
+    assert t["BM"] == 256
+    m = attnio.attn_io_model(1, H, N, d, 2, True)
+    row = d * 2
+    l2_keys = 4 * 1024 * 1024 // (2 * row)
+    resident = 32 * 256  # one 256-row workgroup per CU, 32 CUs per XCD
+    gens = [N - g * resident for g in range(N // resident)]
+    kv_keys = gens[0] + sum(k - min(l2_keys, k) for k in gens[1:])
+    want = H * (2 * row * N + 2 * row * kv_keys)
+    assert m["t_l2"] == want
+    assert abs(m["t_l2"] / m["t_min"] - 1.375) < 1e-3
+    # non-causal: one generation per 8192 rows, no reuse across generations
+    nc = attnio.attn_io_model(1, 16, 8192, d, 2, False)
+    assert nc["t_l2"] == 16 * (2 * row * 8192 + 2 * row * 8192)
