@@ -33,7 +33,6 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (no sparsity)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 DEFAULT_WORKLOAD = "bf16_causal_h32_n32k_d128"
 KERNEL_SOURCE = os.path.join(ROOT, "exact_long_sequence_amd", "csrc", "attn_fwd_bf16.hip")
-COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "attn_fwd_bf16_causal_b1_h32_n32k_d128_counters.md")
 
 
 def kernel_source_digest() -> str:
@@ -41,12 +40,20 @@ def kernel_source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, or None when it is
-    missing, for another workload, or taken on a different kernel source."""
-    if workload != DEFAULT_WORKLOAD or not os.path.exists(COUNTER_SUMMARY):
+def counter_summary_path(w) -> str:
+    """profiles/ summary of the HBM counters taken on workload w (bf16 kernel)."""
+    kind = "causal" if w.causal else ("padded" if w.padded else "full")
+    return os.path.join(ROOT, "profiles",
+                        f"attn_fwd_bf16_{kind}_b{w.B}_h{w.H}_n{w.N // 1024}k_d{w.d}_counters.md")
+
+
+def committed_traffic(w):
+    """HBM bytes per launch from the committed counter summary of workload w, or
+    None when there is none or it was taken on a different kernel source."""
+    path = counter_summary_path(w)
+    if w.dtype != "bf16" or not os.path.exists(path):
         return None
-    text = open(COUNTER_SUMMARY).read()
+    text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_sha and m_b) or m_sha.group(1) != kernel_source_digest():
@@ -180,7 +187,7 @@ def main() -> int:
     flops = model["flops"]
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else 157.3
-    traffic = committed_traffic(w.name)
+    traffic = committed_traffic(w)
     result = {
         "metric": "attention fwd TFLOP/s (algorithmic 4*d per visible query-key pair)",
         "value": tflops,
