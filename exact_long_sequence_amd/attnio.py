@@ -20,8 +20,8 @@ _lib = None
 
 ATTN_OK = 0
 
-__all__ = ["attn_fwd", "attn_fwd_f32", "attn_strerror", "attn_version", "attn_query_tiling",
-           "attn_io_model", "library_path", "load_library"]
+__all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_strerror",
+           "attn_version", "attn_query_tiling", "attn_io_model", "library_path", "load_library"]
 
 
 def library_path() -> str:
@@ -41,6 +41,10 @@ def load_library() -> ctypes.CDLL:
     for name in ("attn_fwd", "attn_fwd_f32"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+        fn.restype = i32
+    for name in ("attn_fwd_lse", "attn_fwd_f32_lse"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
         fn.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -105,7 +109,7 @@ def _check(q, k, v, dtype):
         raise ValueError("q, k, v must be on one device")
 
 
-def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out):
+def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out, lse=False):
     lib = load_library()
     _check(q, k, v, dtype)
     B, H, N, d = q.shape
@@ -115,6 +119,15 @@ def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out):
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous tensor like q")
+    lse_t = None
+    if lse is not False:
+        if lse is None or lse is True:
+            lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        else:
+            lse_t = lse
+            if (lse_t.shape != (B, H, N) or lse_t.dtype != torch.float32 or not lse_t.is_contiguous()
+                    or lse_t.device != q.device):
+                raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     kv_ptr = None
     if kv_len is not None:
         if not isinstance(kv_len, torch.Tensor):
@@ -127,11 +140,13 @@ def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out):
         kv_ptr = kv_len.data_ptr()
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        rc = getattr(lib, fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   B, H, N, d, float(scale), int(bool(causal)), kv_ptr, stream)
+        ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()]
+        if lse_t is not None:
+            ptrs.append(lse_t.data_ptr())
+        rc = getattr(lib, fn_name)(*ptrs, B, H, N, d, float(scale), int(bool(causal)), kv_ptr, stream)
     if rc != ATTN_OK:
         raise RuntimeError(f"{fn_name}: {attn_strerror(rc)} (code {rc})")
-    return out
+    return out if lse_t is None else (out, lse_t)
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
@@ -149,3 +164,20 @@ def attn_fwd_f32(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: b
                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """fp32 exact attention forward; same contract as attn_fwd."""
     return _call("attn_fwd_f32", torch.float32, q, k, v, causal, kv_len, scale, out)
+
+
+def attn_fwd_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                 kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """bf16 forward that also returns the per-row log-sum-exp (float32 [B, H, N],
+    -inf for rows without a visible key).  Returns (out, lse)."""
+    return _call("attn_fwd_lse", torch.bfloat16, q, k, v, causal, kv_len, scale, out,
+                 lse if lse is not None else None)
+
+
+def attn_fwd_f32_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                     kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """fp32 forward with the log-sum-exp side output; returns (out, lse)."""
+    return _call("attn_fwd_f32_lse", torch.float32, q, k, v, causal, kv_len, scale, out,
+                 lse if lse is not None else None)

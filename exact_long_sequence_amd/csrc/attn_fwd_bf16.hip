@@ -69,6 +69,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTauLog2 = 8.0f;        // shift moves when a row maximum exceeds it by 2^8
 constexpr float kLazySumMax = 65536.f;  // a tile row sum above this recomputes the shift
 
@@ -285,8 +286,8 @@ template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WG_PER_CU, bo
 __global__ __launch_bounds__(64 * WAVES, 2)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
-                          const int32_t* __restrict__ kv_len, int H, int N, float c,
-                          int n_qtiles) {
+                          const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
+                          int N, float c, int n_qtiles) {
   using C = Cfg<D, BN, WAVES, PINGPONG ? 2 : STAGES>;
   static_assert(!PINGPONG || WAVES % 2 == 0, "ping-pong needs two equal wave groups");
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
@@ -540,6 +541,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const u32x2 lp = swap_halves(l_run);
   const float l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // log-sum-exp: sum_j 2^(c s_j) = 2^m_run * l, so ln(sum_j e^(scale s_j)) = (m_run + log2 l) ln 2
+  if (lse != nullptr && half == 0 && qrow < N)
+    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   if (qrow < N) {
     __bf16* orow = Os + (size_t)qrow * D;
 #pragma unroll
@@ -569,7 +573,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, STAGES, PINGPONG, WPC, SNAKE, CAUSAL, NEG>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
-                     a.kv_len, a.H, a.N, c, n_qtiles);
+                     a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
 }
 

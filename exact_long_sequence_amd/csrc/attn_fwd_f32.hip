@@ -24,6 +24,7 @@ namespace attnio {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQ = 16;        // queries per workgroup
 constexpr int kLanes = 16;    // key lanes per query
 constexpr int kBN = 64;       // keys per LDS tile
@@ -32,8 +33,8 @@ template <int D, bool CAUSAL, bool NEG>
 __global__ __launch_bounds__(256)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, float* __restrict__ O,
-                         const int32_t* __restrict__ kv_len, int H, int N, float c,
-                         int n_qtiles) {
+                         const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
+                         int N, float c, int n_qtiles) {
   constexpr int P = D + 4;  // padded LDS row (floats): keeps 16 rows on distinct banks
   __shared__ __attribute__((aligned(16))) float qs[kQ * P];
   __shared__ __attribute__((aligned(16))) float ks[kBN * P];
@@ -139,6 +140,10 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     for (int off = kLanes / 2; off > 0; off /= 2) x += __shfl_xor(x, off, kLanes);
     acc[e] = x;
   }
+  // log-sum-exp: sum_j 2^(c s_j) = 2^(c m_all) * l (m_all is the raw-score
+  // extreme, c * m_all the largest exponent whatever the sign of c)
+  if (lse != nullptr && kl == 0 && qrow < N)
+    lse[(size_t)bh * N + qrow] = l > 0.f ? (m_all * c + log2f(l)) * kLn2 : -INFINITY;
   if (qrow < N) {
     constexpr int PER = D / kLanes;
 #pragma unroll
@@ -158,7 +163,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   if (c == 0.f) c = FLT_MIN;
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(256), 0,
                      stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
-                     a.kv_len, a.H, a.N, c, n_qtiles);
+                     a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
 }
 

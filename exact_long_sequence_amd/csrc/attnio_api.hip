@@ -47,6 +47,12 @@ bool overlaps(const void* a, const void* b, size_t bytes) {
   return x < y + bytes && y < x + bytes;
 }
 
+// [a, a + na) and [b, b + nb) intersect
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
 int validate(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
              float scale, int elem) {
   if (!Q || !K || !V || !O) return ATTN_E_NULL;
@@ -61,12 +67,21 @@ int validate(const void* Q, const void* K, const void* V, void* O, int B, int H,
   return ATTN_OK;
 }
 
-int run(bool bf16, const void* Q, const void* K, const void* V, void* O, int B, int H, int N,
-        int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* lse, bool want_lse,
+        int B, int H, int N, int d, float scale, int causal, const int32_t* kv_len, void* stream) {
   const int rc = validate(Q, K, V, O, B, H, N, d, scale, bf16 ? 2 : 4);
   if (rc != ATTN_OK) return rc;
+  if (want_lse) {
+    if (lse == nullptr) return ATTN_E_NULL;
+    if (((uintptr_t)lse) & 3u) return ATTN_E_ALIGN;
+    const size_t lb = (size_t)B * H * N * sizeof(float);
+    const size_t tb = (size_t)B * H * N * d * (bf16 ? 2 : 4);
+    if (ranges_overlap(lse, lb, Q, tb) || ranges_overlap(lse, lb, K, tb) ||
+        ranges_overlap(lse, lb, V, tb) || ranges_overlap(lse, lb, O, tb))
+      return ATTN_E_ALIAS;
+  }
   if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
-  attnio::FwdArgs a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0};
+  attnio::FwdArgs a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0, want_lse ? lse : nullptr};
   if (log_enabled()) {
     attnio::Tiling t{};
     if (bf16 && attnio::bf16_tiling(d, causal, &t))
@@ -98,12 +113,22 @@ extern "C" {
 
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
              float scale, int causal, const int32_t* kv_len, void* stream) {
-  return run(true, Q, K, V, O, B, H, N, d, scale, causal, kv_len, stream);
+  return run(true, Q, K, V, O, nullptr, false, B, H, N, d, scale, causal, kv_len, stream);
 }
 
 int attn_fwd_f32(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
                  float scale, int causal, const int32_t* kv_len, void* stream) {
-  return run(false, Q, K, V, O, B, H, N, d, scale, causal, kv_len, stream);
+  return run(false, Q, K, V, O, nullptr, false, B, H, N, d, scale, causal, kv_len, stream);
+}
+
+int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                 int N, int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+  return run(true, Q, K, V, O, LSE, true, B, H, N, d, scale, causal, kv_len, stream);
+}
+
+int attn_fwd_f32_lse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                     int N, int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+  return run(false, Q, K, V, O, LSE, true, B, H, N, d, scale, causal, kv_len, stream);
 }
 
 const char* attn_strerror(int code) {

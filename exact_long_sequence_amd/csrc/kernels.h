@@ -17,6 +17,7 @@ struct FwdArgs {
   int B, H, N, d;
   float scale;
   int causal;
+  float* lse;             // device float[B, H, N] or nullptr (log-sum-exp side output)
 };
 
 // Tile configuration of the bf16 streaming kernel for head size d.

@@ -73,6 +73,21 @@ int attn_fwd_f32(const void* Q, const void* K, const void* V, void* O,
                  int B, int H, int N, int d, float scale, int causal,
                  const int32_t* kv_len, void* stream);
 
+/* Forward with the log-sum-exp side output ("IO-Aware Algorithms", How it
+ * works: the backward pass recomputes the probabilities from Q, K, V and this
+ * per-row statistic instead of storing them).  Same contract as attn_fwd /
+ * attn_fwd_f32, plus:
+ *   LSE   DEVICE float[B, H, N], written for every row: the natural log of
+ *         sum_j exp(scale * q_i . k_j) over the visible keys j, or -inf for a
+ *         row with no visible key.  It must not overlap Q, K, V or O.
+ * Returns ATTN_E_NULL if LSE is NULL, ATTN_E_ALIAS if it overlaps. */
+int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int B, int H, int N, int d, float scale, int causal,
+                 const int32_t* kv_len, void* stream);
+int attn_fwd_f32_lse(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const int32_t* kv_len, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_strerror(int code);
 

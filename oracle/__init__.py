@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     allowed_mask,
     attention_fp64,
     attention_full_fp64,
+    attention_lse_fp64,
     attention_rows_fp64,
     decode_bf16_bits,
     effective_kv_len,

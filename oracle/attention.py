@@ -48,6 +48,7 @@ __all__ = [
     "attention_rows_fp64",
     "attention_full_fp64",
     "allowed_key_count",
+    "attention_lse_fp64",
 ]
 
 
@@ -208,3 +209,30 @@ def allowed_key_count(rows_i: np.ndarray, L: int, N: int, causal: bool) -> np.nd
     if causal:
         return np.minimum(i + 1, L)
     return np.full(i.shape, min(L, N), dtype=np.int64)
+
+
+def attention_lse_fp64(q, k, v, scale: float, causal: bool = False, kv_len=None,
+                       kind: str = "bf16", rows=None, chunk: int = 1024) -> np.ndarray:
+    """Log-sum-exp of each query row's scaled, masked scores, in fp64:
+    lse_i = ln sum_j exp(scale * q_i . k_j) over the keys j visible to row i, or
+    -inf for a row with no visible key.  This is the per-row statistic the
+    backward pass recomputes the probabilities from ("IO-Aware Algorithms",
+    How it works, recomputation).  rows: None for [B, H, N], or flat
+    (b*H + h)*N + i indices (returns [len(rows)])."""
+    qa, ka, va = np.asarray(q), np.asarray(k), np.asarray(v)
+    B, H, N, d = qa.shape
+    Ls = effective_kv_len(kv_len, B, N)
+    flat = (np.arange(B * H * N, dtype=np.int64) if rows is None
+            else np.asarray(rows, dtype=np.int64).reshape(-1))
+    if flat.size and (flat.min() < 0 or flat.max() >= B * H * N):
+        raise ValueError("row index out of range")
+    out = np.empty(flat.shape[0], dtype=np.float64)
+    bh = flat // N
+    for s in np.unique(bh):
+        sel = np.nonzero(bh == s)[0]
+        b, h = divmod(int(s), H)
+        _, _, lse = attention_rows_fp64(to_fp64(qa[b, h], kind), to_fp64(ka[b, h], kind),
+                                        to_fp64(va[b, h], kind), flat[sel] % N, scale, causal,
+                                        int(Ls[b]), chunk, want_p=True)
+        out[sel] = lse
+    return out if rows is not None else out.reshape(B, H, N)

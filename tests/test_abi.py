@@ -30,8 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"attn_fwd", "attn_fwd_f32", "attn_strerror", "attn_version", "attn_query_tiling",
-            "attn_io_model"} <= names
+    assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_strerror",
+            "attn_version", "attn_query_tiling", "attn_io_model"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -62,6 +62,19 @@ def _call(lib, name, q=0x1000, k=0x2000000, v=0x4000000, o=0x6000000, B=1, H=1, 
           scale=0.125, causal=0):
     fn = getattr(lib, name)
     return fn(q, k, v, o, B, H, N, d, ctypes.c_float(scale), causal, None, None)
+
+
+@pytest.mark.parametrize("name", ["attn_fwd_lse", "attn_fwd_f32_lse"])
+def test_lse_entry_argument_errors(lib, name):
+    fn = getattr(lib, name)
+
+    def call(lse, q=0x1000, o=0x6000000):
+        return fn(q, 0x2000000, 0x4000000, o, lse, 1, 1, 16, 64, ctypes.c_float(0.125), 0, None, None)
+    assert call(None) == -1                      # LSE is required here
+    assert call(0x8000002) == -4                 # not 4-byte aligned
+    assert call(0x1000 + 16) == -7               # LSE overlaps Q
+    assert call(0x6000000 + 4) == -7             # LSE overlaps O
+    assert call(0x8000000, q=None) == -1         # the usual checks still apply
 
 
 @pytest.mark.parametrize("name", ["attn_fwd", "attn_fwd_f32"])

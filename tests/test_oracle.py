@@ -354,3 +354,56 @@ def test_mutants_are_caught(monkeypatch):
     assert not _pins_pass()
     monkeypatch.setattr(oa, "attention_rows_fp64", real_rows)
     assert _pins_pass()
+
+
+# --------------------------------------------------------------------------
+# log-sum-exp side output: brute force with math.exp / math.fsum / math.log
+# --------------------------------------------------------------------------
+def brute_force_lse(q, k, scale, causal, kv_len):
+    B, H, N, d = q.shape
+    out = np.full((B, H, N), -np.inf)
+    s = float(np.float32(scale))
+    for b in range(B):
+        L = N if kv_len is None else max(0, min(int(kv_len[b]), N))
+        for h in range(H):
+            for i in range(N):
+                keys = [j for j in range(N) if j < L and (not causal or j <= i)]
+                if keys:
+                    out[b, h, i] = math.log(math.fsum(
+                        math.exp(s * math.fsum(float(q[b, h, i, t]) * float(k[b, h, j, t])
+                                               for t in range(d))) for j in keys))
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 3, 8, 13])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("padded", [False, True])
+def test_lse_brute_force_tiny(N, causal, padded):
+    B, H, d = 2, 2, 4
+    seed = 7000 + 10 * N + 2 * causal + padded
+    q, k, v = (_rand((B, H, N, d), seed + t) for t in range(3))
+    kv_len = np.array([0, N]) if padded else None
+    got = oracle.attention_lse_fp64(q, k, v, 0.5, causal, kv_len, kind="f64")
+    ref = brute_force_lse(q, k, 0.5, causal, kv_len)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    np.testing.assert_allclose(got[fin], ref[fin], rtol=0, atol=1e-12)
+    # rows selected by flat index give the same values
+    rows = np.array([0, B * H * N - 1, (B * H * N) // 2])
+    np.testing.assert_allclose(
+        oracle.attention_lse_fp64(q, k, v, 0.5, causal, kv_len, kind="f64", rows=rows),
+        got.reshape(-1)[rows], rtol=0, atol=1e-13)
+
+
+def test_lse_closed_forms():
+    """Zero scale: lse = ln(number of visible keys).  Equal scores c over n keys:
+    lse = c + ln n (q = e_0, k_j = (1, ...))."""
+    B, H, N, d = 1, 1, 9, 3
+    q = _rand((B, H, N, d), 1)
+    k = _rand((B, H, N, d), 2)
+    lse = oracle.attention_lse_fp64(q, k, k, 0.0, True, None, kind="f64")
+    np.testing.assert_allclose(lse[0, 0], np.log(np.arange(1, N + 1)), atol=1e-14)
+    q1 = np.zeros((B, H, N, d)); q1[..., 0] = 1.0
+    k1 = np.zeros((B, H, N, d)); k1[..., 0] = 2.0
+    lse1 = oracle.attention_lse_fp64(q1, k1, k1, 0.75, False, [5], kind="f64")
+    np.testing.assert_allclose(lse1[0, 0], 0.75 * 2.0 + np.log(5.0), atol=1e-14)
