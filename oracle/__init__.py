@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for exact attention forward -- test infrastructure only.
+"""fp64 CPU oracle for exact attention (forward, lse, backward) -- test infrastructure only.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP path.
@@ -9,6 +9,8 @@ from .attention import (  # noqa: F401
     attention_fp64,
     attention_full_fp64,
     attention_lse_fp64,
+    attention_bwd_fp64,
+    attention_bwd_rows_fp64,
     attention_rows_fp64,
     decode_bf16_bits,
     effective_kv_len,

@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for exact self-attention forward.
+"""Plain fp64 CPU oracle for exact self-attention (forward, its log-sum-exp
+side output, and the backward gradients).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
 module: only the tests, the smoke check and the CPU-baseline leg of the
@@ -49,6 +50,8 @@ __all__ = [
     "attention_full_fp64",
     "allowed_key_count",
     "attention_lse_fp64",
+    "attention_bwd_fp64",
+    "attention_bwd_rows_fp64",
 ]
 
 
@@ -236,3 +239,49 @@ def attention_lse_fp64(q, k, v, scale: float, causal: bool = False, kv_len=None,
                                         int(Ls[b]), chunk, want_p=True)
         out[sel] = lse
     return out if rows is not None else out.reshape(B, H, N)
+
+
+def attention_bwd_rows_fp64(Qf: np.ndarray, Kf: np.ndarray, Vf: np.ndarray, dOf: np.ndarray,
+                            scale: float, causal: bool, L: int):
+    """Gradients of one (batch, head) slice, all rows, in fp64.
+
+    With S = s Q K^T masked, P = softmax(S) and O = P V, the loss gradient dO
+    gives (the chain rule through the operator graph, as the backward pass of
+    "IO-Aware Algorithms", How it works, recomputes it from Q, K, V):
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))        (softmax Jacobian, row by row)
+        dQ = s dS K,   dK = s dS^T Q
+    P is materialised here on purpose; masked entries are exactly 0."""
+    N = Qf.shape[0]
+    s64 = float(np.float32(scale))
+    S = s64 * (Qf @ Kf.T)
+    ok = allowed_mask(np.arange(N), Kf.shape[0], L, causal)
+    P, _ = _softmax_rows(S, ok)
+    dV = P.T @ dOf
+    dP = dOf @ Vf.T
+    Dr = (P * dP).sum(axis=1, keepdims=True)
+    dS = P * (dP - Dr)
+    dQ = s64 * (dS @ Kf)
+    dK = s64 * (dS.T @ Qf)
+    return dQ, dK, dV
+
+
+def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool = False, kv_len=None,
+                       kind: str = "bf16"):
+    """Exact attention backward in fp64 for [B, H, N, d] inputs: returns
+    (dQ, dK, dV), each float64 [B, H, N, d].  q, k, v, do are of the given kind
+    ('bf16' uint16 bit patterns, 'f32' or 'f64').  Keys past kv_len get zero
+    gradients; rows without a visible key contribute nothing."""
+    qa, ka, va, da = (np.asarray(t) for t in (q, k, v, do))
+    if qa.ndim != 4 or not (qa.shape == ka.shape == va.shape == da.shape):
+        raise ValueError("q, k, v, do must share one [B,H,N,d] shape")
+    B, H, N, d = qa.shape
+    Ls = effective_kv_len(kv_len, B, N)
+    dQ = np.empty((B, H, N, d)); dK = np.empty((B, H, N, d)); dV = np.empty((B, H, N, d))
+    for b in range(B):
+        for h in range(H):
+            dQ[b, h], dK[b, h], dV[b, h] = attention_bwd_rows_fp64(
+                to_fp64(qa[b, h], kind), to_fp64(ka[b, h], kind), to_fp64(va[b, h], kind),
+                to_fp64(da[b, h], kind), scale, causal, int(Ls[b]))
+    return dQ, dK, dV

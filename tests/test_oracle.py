@@ -407,3 +407,50 @@ def test_lse_closed_forms():
     k1 = np.zeros((B, H, N, d)); k1[..., 0] = 2.0
     lse1 = oracle.attention_lse_fp64(q1, k1, k1, 0.75, False, [5], kind="f64")
     np.testing.assert_allclose(lse1[0, 0], 0.75 * 2.0 + np.log(5.0), atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# backward: central finite differences of the forward oracle (an independent
+# check of every gradient formula), plus the zero-gradient rules for masked keys
+# --------------------------------------------------------------------------
+def _loss(q, k, v, do, scale, causal, kv_len):
+    return float((oracle.attention_fp64(q, k, v, scale, causal, kv_len, kind="f64") * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("padded", [False, True])
+def test_backward_matches_finite_differences(causal, padded):
+    B, H, N, d = 2, 1, 6, 3
+    seed = 9100 + 2 * causal + padded
+    q, k, v, do = (_rand((B, H, N, d), seed + t, sd=0.9) for t in range(4))
+    kv_len = np.array([4, 6]) if padded else None
+    scale = 0.8
+    dq, dk, dv = oracle.attention_bwd_fp64(q, k, v, do, scale, causal, kv_len, kind="f64")
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, scale, causal, kv_len)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, scale, causal, kv_len)
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=2e-8, err_msg=f"d{name}")
+    if padded:
+        assert (dk[0, :, 4:] == 0).all() and (dv[0, :, 4:] == 0).all()
+
+
+def test_backward_invariants():
+    """Each row of dS sums to zero, so dQ is unchanged when every key row of K
+    shifts by the same vector; dV sums to sum_i dO_i over rows that see keys."""
+    B, H, N, d = 1, 2, 7, 4
+    q, k, v, do = (_rand((B, H, N, d), 9300 + t) for t in range(4))
+    dq, dk, dv = oracle.attention_bwd_fp64(q, k, v, do, 0.6, True, None, kind="f64")
+    shift = np.random.default_rng(5).normal(size=(1, 1, 1, d))
+    dq2, _, _ = oracle.attention_bwd_fp64(q, k + shift, v, do, 0.6, True, None, kind="f64")
+    np.testing.assert_allclose(dq, dq2, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)   # sum_j dK_j = s sum_i (sum_j dS_ij) q_i = 0
