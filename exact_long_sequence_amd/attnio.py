@@ -20,8 +20,9 @@ _lib = None
 
 ATTN_OK = 0
 
-__all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_strerror",
-           "attn_version", "attn_query_tiling", "attn_io_model", "library_path", "load_library"]
+__all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
+           "attn_bwd_workspace_bytes", "attn_strerror", "attn_version", "attn_query_tiling",
+           "attn_io_model", "library_path", "load_library"]
 
 
 def library_path() -> str:
@@ -46,6 +47,10 @@ def load_library() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
         fn.restype = i32
+    lib.attn_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -109,6 +114,20 @@ def _check(q, k, v, dtype):
         raise ValueError("q, k, v must be on one device")
 
 
+def _kv_len_ptr(kv_len, B, device):
+    """Returns (tensor kept alive, device pointer or None)."""
+    if kv_len is None:
+        return None, None
+    if not isinstance(kv_len, torch.Tensor):
+        kv_len = torch.tensor(kv_len, dtype=torch.int32)
+    if kv_len.device != device or kv_len.dtype != torch.int32:
+        kv_len = kv_len.to(device=device, dtype=torch.int32)
+    kv_len = kv_len.contiguous()
+    if kv_len.numel() != B:
+        raise ValueError(f"kv_len must have B={B} entries, got {kv_len.numel()}")
+    return kv_len, kv_len.data_ptr()
+
+
 def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out, lse=False):
     lib = load_library()
     _check(q, k, v, dtype)
@@ -128,16 +147,7 @@ def _call(fn_name, dtype, q, k, v, causal, kv_len, scale, out, lse=False):
             if (lse_t.shape != (B, H, N) or lse_t.dtype != torch.float32 or not lse_t.is_contiguous()
                     or lse_t.device != q.device):
                 raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
-    kv_ptr = None
-    if kv_len is not None:
-        if not isinstance(kv_len, torch.Tensor):
-            kv_len = torch.tensor(kv_len, dtype=torch.int32)
-        if kv_len.device != q.device or kv_len.dtype != torch.int32:
-            kv_len = kv_len.to(device=q.device, dtype=torch.int32)
-        kv_len = kv_len.contiguous()
-        if kv_len.numel() != B:
-            raise ValueError(f"kv_len must have B={B} entries, got {kv_len.numel()}")
-        kv_ptr = kv_len.data_ptr()
+    kv_len, kv_ptr = _kv_len_ptr(kv_len, B, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()]
@@ -181,3 +191,54 @@ def attn_fwd_f32_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     """fp32 forward with the log-sum-exp side output; returns (out, lse)."""
     return _call("attn_fwd_f32_lse", torch.float32, q, k, v, causal, kv_len, scale, out,
                  lse if lse is not None else None)
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    """Device workspace bytes attn_bwd needs (0 for non-positive sizes)."""
+    return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             dout: torch.Tensor, lse: torch.Tensor, *, causal: bool = False,
+             kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+             dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+             dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """bf16 attention backward from the forward's (q, k, v, o, lse) and dout.
+
+    causal, kv_len and scale must be those of the forward that produced o and
+    lse.  Returns (dq, dk, dv).  workspace: optional uint8 device tensor of at
+    least attn_bwd_workspace_bytes(B, H, N) bytes."""
+    lib = load_library()
+    _check(q, k, v, torch.bfloat16)
+    _check(o, dout, q, torch.bfloat16)
+    B, H, N, d = q.shape
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor like q")
+        grads.append(t)
+    need = attn_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif (workspace.device != q.device or not workspace.is_contiguous()
+          or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace must be a contiguous device buffer of >= {need} bytes")
+    kv_len, kv_ptr = _kv_len_ptr(kv_len, B, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                          lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                          grads[2].data_ptr(), workspace.data_ptr(), B, H, N, d, float(scale),
+                          int(bool(causal)), kv_ptr, stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_bwd: {attn_strerror(rc)} (code {rc})")
+    return tuple(grads)

@@ -131,6 +131,46 @@ int attn_fwd_f32_lse(const void* Q, const void* K, const void* V, void* O, float
   return run(false, Q, K, V, O, LSE, true, B, H, N, d, scale, causal, kv_len, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return attnio::bwd_workspace_bytes(B, H, N);
+}
+
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, void* dQ, void* dK, void* dV, void* workspace, int B, int H, int N,
+             int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+  if (!dO || !LSE || !dQ || !dK || !dV || !workspace) return ATTN_E_NULL;
+  int rc = validate(Q, K, V, dQ, B, H, N, d, scale, 2);
+  if (rc != ATTN_OK) return rc;
+  if (!O) return ATTN_E_NULL;
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const size_t wb = attnio::bwd_workspace_bytes(B, H, N);
+  if ((((uintptr_t)O | (uintptr_t)dO | (uintptr_t)dK | (uintptr_t)dV | (uintptr_t)workspace) & 15u) ||
+      ((uintptr_t)LSE & 3u))
+    return ATTN_E_ALIGN;
+  // outputs must not overlap any input, each other, or the workspace
+  const void* ins[6] = {Q, K, V, O, dO, LSE};
+  const size_t in_b[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dQ, dK, dV, workspace};
+  const size_t out_b[4] = {tb, tb, tb, wb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return ATTN_E_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return ATTN_E_ALIAS;
+  }
+  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  attnio::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, kv_len, B, H, N, d, scale,
+                    causal ? 1 : 0};
+  const hipError_t e = attnio::launch_bwd_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (log_enabled()) fprintf(stderr, "[attnio] backward launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
 const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";

@@ -30,7 +30,27 @@ struct Tiling {
   int wg_per_cu;  // workgroups resident per CU (register and LDS bound)
 };
 
+// Backward launch parameters (device pointers validated by the front end).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;               // bwd_workspace_bytes(B, H, N) bytes
+  const int32_t* kv_len;
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
 bool bf16_tiling(int d, int causal, Tiling* t);
+size_t bwd_workspace_bytes(int B, int H, int N);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 

@@ -40,6 +40,7 @@
 #ifndef ATTNIO_H
 #define ATTNIO_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -87,6 +88,33 @@ int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* LS
 int attn_fwd_f32_lse(const void* Q, const void* K, const void* V, void* O, float* LSE,
                      int B, int H, int N, int d, float scale, int causal,
                      const int32_t* kv_len, void* stream);
+
+/* bf16 attention backward ("IO-Aware Algorithms", How it works: the backward
+ * pass recomputes the probabilities from Q, K, V and the forward's per-row
+ * log-sum-exp instead of reading a stored N x N matrix).  Given the forward's
+ * inputs Q, K, V, its output O and LSE (from attn_fwd_lse, same scale, causal
+ * and kv_len), and the output gradient dO, it writes
+ *   dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q,
+ * with P_ij = exp(scale q_i.k_j - LSE_i) on visible pairs (0 elsewhere),
+ * dS = P * (dO V^T - D) and D_i = dO_i . O_i.
+ * Q, K, V, O, dO, dQ, dK, dV are bf16 [B, H, N, d] device tensors laid out as
+ * for attn_fwd; LSE is a device float[B, H, N].  Keys past kv_len get zero dK
+ * and dV.  workspace: a device buffer of attn_bwd_workspace_bytes(B, H, N)
+ * bytes, 16-byte aligned, owned by the caller; its contents on entry do not
+ * matter and on return are unspecified.  dQ, dK, dV and the workspace must not
+ * overlap each other or any input.  Products run on bf16 matrix cores with
+ * fp32 accumulation; P and dS are rounded to bf16 as operands; the gradients
+ * are rounded to bf16 once.  Three kernels are enqueued on `stream`; nothing
+ * is allocated and nothing synchronises.  Returns 0 or an ATTN_E* code
+ * (checks as for attn_fwd, plus NULL and alias checks on every buffer). */
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, void* dQ, void* dK, void* dV, void* workspace,
+             int B, int H, int N, int d, float scale, int causal,
+             const int32_t* kv_len, void* stream);
+
+/* Bytes of device workspace attn_bwd needs for B x H heads of N rows (host
+ * only; 0 for non-positive sizes). */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_strerror(int code);

@@ -30,8 +30,9 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = set(declared_functions())
-    assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_strerror",
-            "attn_version", "attn_query_tiling", "attn_io_model"} <= names
+    assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
+            "attn_bwd_workspace_bytes", "attn_strerror", "attn_version", "attn_query_tiling",
+            "attn_io_model"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -75,6 +76,40 @@ def test_lse_entry_argument_errors(lib, name):
     assert call(0x1000 + 16) == -7               # LSE overlaps Q
     assert call(0x6000000 + 4) == -7             # LSE overlaps O
     assert call(0x8000000, q=None) == -1         # the usual checks still apply
+
+
+def test_bwd_workspace_bytes(lib):
+    # two fp32 row statistics per row, rows padded to 64 per head
+    assert attnio.attn_bwd_workspace_bytes(1, 1, 1) == 2 * 64 * 4
+    assert attnio.attn_bwd_workspace_bytes(2, 3, 130) == 2 * 6 * 192 * 4
+    assert attnio.attn_bwd_workspace_bytes(0, 1, 1) == 0
+    assert attnio.attn_bwd_workspace_bytes(1, 1, -5) == 0
+
+
+def test_bwd_entry_argument_errors(lib):
+    # tensors of B*H*N*d = 1*1*16*64 bf16 = 2 KiB, spaced 1 MiB apart
+    base = {"Q": 0x100000, "K": 0x200000, "V": 0x300000, "O": 0x400000, "dO": 0x500000,
+            "LSE": 0x600000, "dQ": 0x700000, "dK": 0x800000, "dV": 0x900000, "ws": 0xA00000}
+
+    def call(d=64, N=16, **over):
+        p = dict(base, **over)
+        return lib.attn_bwd(p["Q"], p["K"], p["V"], p["O"], p["dO"], p["LSE"], p["dQ"], p["dK"],
+                            p["dV"], p["ws"], 1, 1, N, d, ctypes.c_float(0.125), 0, None, None)
+    for name in base:
+        assert call(**{name: None}) == -1, name
+    assert call(d=96) == -2
+    assert call(N=0) == -3
+    for name in ("Q", "K", "V", "O", "dO", "dQ", "dK", "dV", "ws"):
+        assert call(**{name: base[name] + 8}) == -4, name
+    assert call(LSE=base["LSE"] + 2) == -4
+    assert call(dQ=base["Q"] + 1024) == -7           # output overlaps an input
+    assert call(dK=base["dO"]) == -7
+    assert call(dV=base["LSE"] + 16) == -7
+    assert call(ws=base["dQ"] + 512) == -7           # workspace overlaps an output
+    assert call(dK=base["dV"] + 1024) == -7          # outputs overlap each other
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert call() == -6
 
 
 @pytest.mark.parametrize("name", ["attn_fwd", "attn_fwd_f32"])

@@ -1,0 +1,138 @@
+"""GPU parity of the bf16 attention backward (attn_bwd) against the fp64 oracle,
+through the C ABI.
+
+The forward runs first on the GPU (attn_fwd_lse) to produce O and the
+log-sum-exp, exactly as a training step would feed the backward; the oracle
+computes the gradients from Q, K, V and dO alone, in fp64.
+
+Tolerance, per gradient G in {dQ, dK, dV} and per case:
+    max |G - G_ref| <= 2.5e-2 * max |G_ref|,   mean |G - G_ref| <= 1e-2 * mean |G_ref|.
+Derivation: every gradient is a sum of products whose factors P, dS and the
+output are each rounded to bf16 once (relative error <= 2^-9 each) and whose
+D_i = dO_i . O_i uses the bf16 forward output (relative error <= 2^-9); the
+sum of such errors is bounded by a few times 2^-9 ~ 2e-3 of the sum of the
+absolute terms, which for these inputs stays within a few times max |G_ref|.
+A CPU model of exactly these roundings gives max errors up to 0.93% of
+max |G_ref| and mean errors up to 0.45% of mean |G_ref| on the shapes below
+(peaked softmax included), so the bounds leave a margin of 2 to 3.  Keys past
+kv_len must get exactly zero dK and dV, and rows with no visible key exactly
+zero dQ.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_long_sequence_amd import attnio
+from exact_long_sequence_amd.inputs import make_inputs, oracle_view
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL_MAX = 2.5e-2
+TOL_MEAN = 1e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dout(shape, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _check_grad(got, want, label):
+    got = got.double().cpu().numpy()
+    assert np.isfinite(got).all(), f"{label}: non-finite gradient"
+    err = np.abs(got - want)
+    ref_max = float(np.abs(want).max(initial=0.0))
+    ref_mean = float(np.abs(want).mean()) if want.size else 0.0
+    mx, mn = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    assert mx <= TOL_MAX * ref_max + 1e-6, f"{label}: max_err={mx:.3e} max|ref|={ref_max:.3e}"
+    assert mn <= TOL_MEAN * ref_mean + 1e-7, f"{label}: mean_err={mn:.3e} mean|ref|={ref_mean:.3e}"
+
+
+def _run_case(B, H, N, d, causal, padded, seed, q_mul=1.0, kv_lo=0):
+    q, k, v, kv = make_inputs(B, H, N, d, "bf16", seed, padded=padded, q_mul=q_mul,
+                              kv_lo=kv_lo if padded else None)
+    do = _dout(q.shape, seed)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    _log(f"bwd case B={B} H={H} N={N} d={d} causal={causal} padded={padded} q_mul={q_mul} "
+         f"seed={seed} kv_len={None if kv is None else kv.tolist()}")
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    kvd = None if kv is None else kv.to(DEV)
+    o, lse = attnio.attn_fwd_lse(qd, kd, vd, causal=causal, kv_len=kvd, scale=scale)
+    dq, dk, dv = attnio.attn_bwd(qd, kd, vd, o, dod, lse, causal=causal, kv_len=kvd, scale=scale)
+    torch.cuda.synchronize()
+    kv_np = None if kv is None else kv.numpy()
+    want = oracle.attention_bwd_fp64(oracle_view(q), oracle_view(k), oracle_view(v), oracle_view(do),
+                                     scale, causal, kv_np, kind="bf16")
+    for name, g, w in zip(("dQ", "dK", "dV"), (dq, dk, dv), want):
+        _check_grad(g, w, f"{name} N={N} d={d} causal={causal} padded={padded}")
+    if kv is not None:
+        for b in range(B):
+            L = int(kv[b])
+            assert torch.count_nonzero(dk[b, :, L:]).item() == 0, "dK past kv_len is not zero"
+            assert torch.count_nonzero(dv[b, :, L:]).item() == 0, "dV past kv_len is not zero"
+            if L == 0:
+                assert torch.count_nonzero(dq[b]).item() == 0, "dQ of a row without keys is not zero"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("padded", [False, True])
+def test_bwd_small_sweep(d, causal, padded):
+    # N spans a single row, ragged tails of the 64-row and 128-row tiles and
+    # several tiles of both loops
+    for N in (1, 65, 300, 1000):
+        _run_case(2, 2, N, d, causal, padded, seed=900 + N + 3 * d + 7 * causal + 11 * padded)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_peaked_softmax(d):
+    # Q x 8: near one-hot rows, the regime where P's bf16 rounding matters most
+    _run_case(2, 2, 700, d, False, True, seed=950 + d, q_mul=8.0, kv_lo=700 // 4)
+    _run_case(1, 2, 513, d, True, False, seed=960 + d, q_mul=8.0)
+
+
+def test_bwd_empty_keys_and_errors():
+    # every key masked in one batch: zero gradients there, finite elsewhere
+    q, k, v, _ = make_inputs(2, 2, 130, 128, "bf16", 977)
+    do = _dout(q.shape, 977)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    kv = torch.tensor([0, 130], dtype=torch.int32, device=DEV)
+    o, lse = attnio.attn_fwd_lse(qd, kd, vd, kv_len=kv)
+    dq, dk, dv = attnio.attn_bwd(qd, kd, vd, o, dod, lse, kv_len=kv)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq[0]).item() == 0
+    assert torch.count_nonzero(dk[0]).item() == 0 and torch.count_nonzero(dv[0]).item() == 0
+    assert torch.isfinite(dq.float()).all() and torch.count_nonzero(dq[1]).item() > 0
+    with pytest.raises(ValueError):
+        attnio.attn_bwd(qd, kd, vd, o, dod, lse[:, :1].contiguous())
+    with pytest.raises(ValueError):
+        attnio.attn_bwd(qd, kd, vd, o, dod, lse, workspace=torch.empty(8, dtype=torch.uint8, device=DEV))
+    with pytest.raises(RuntimeError):
+        attnio.attn_bwd(qd, kd, vd, o, dod, lse, dq=qd)  # output aliases an input
+
+
+def test_bwd_reuses_caller_buffers():
+    # a second call with caller-provided outputs and a dirty workspace gives
+    # bitwise the same gradients
+    q, k, v, _ = make_inputs(1, 3, 257, 64, "bf16", 978)
+    do = _dout(q.shape, 978)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    o, lse = attnio.attn_fwd_lse(qd, kd, vd, causal=True)
+    g1 = attnio.attn_bwd(qd, kd, vd, o, dod, lse, causal=True)
+    ws = torch.full((attnio.attn_bwd_workspace_bytes(1, 3, 257),), 0x7F, dtype=torch.uint8, device=DEV)
+    outs = [torch.full_like(qd, float("nan")) for _ in range(3)]
+    g2 = attnio.attn_bwd(qd, kd, vd, o, dod, lse, causal=True, dq=outs[0], dk=outs[1], dv=outs[2],
+                         workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
