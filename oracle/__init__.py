@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     attention_lse_fp64,
     attention_bwd_fp64,
     attention_bwd_rows_fp64,
+    attention_bwd_sampled_fp64,
     attention_rows_fp64,
     decode_bf16_bits,
     effective_kv_len,

@@ -52,6 +52,7 @@ __all__ = [
     "attention_lse_fp64",
     "attention_bwd_fp64",
     "attention_bwd_rows_fp64",
+    "attention_bwd_sampled_fp64",
 ]
 
 
@@ -284,4 +285,54 @@ def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool = False, kv_len=N
             dQ[b, h], dK[b, h], dV[b, h] = attention_bwd_rows_fp64(
                 to_fp64(qa[b, h], kind), to_fp64(ka[b, h], kind), to_fp64(va[b, h], kind),
                 to_fp64(da[b, h], kind), scale, causal, int(Ls[b]))
+    return dQ, dK, dV
+
+
+def attention_bwd_sampled_fp64(q, k, v, do, scale: float, causal: bool, kv_len, kind: str,
+                               b: int, h: int, q_rows, k_rows, chunk: int = 512):
+    """Selected gradient rows of ONE (batch, head) slice, for sizes where the
+    dense form does not fit: returns (dQ[q_rows], dK[k_rows], dV[k_rows]).
+
+    The same definitions as attention_bwd_rows_fp64, taken over chunks of query
+    rows so that only a chunk x N block of P, dP and dS ever exists.  A row's
+    softmax, D_i = rowsum(P * dP) and dS need only that row, so each chunk
+    completes its rows; the key-side gradients are sums over query rows,
+        dV_j = sum_i P_ij dO_i,    dK_j = s sum_i dS_ij Q_i,
+    accumulated chunk by chunk for the selected keys j only.  With no key rows
+    selected, only the selected query rows are visited."""
+    qa, ka, va, da = (np.asarray(t) for t in (q, k, v, do))
+    B, H, N, d = qa.shape
+    L = int(effective_kv_len(kv_len, B, N)[b])
+    Qf, Kf, Vf, dOf = (to_fp64(t[b, h], kind) for t in (qa, ka, va, da))
+    s64 = float(np.float32(scale))
+    q_rows = np.asarray(q_rows, dtype=np.int64).reshape(-1)
+    k_rows = np.asarray(k_rows, dtype=np.int64).reshape(-1)
+    dQ = np.zeros((q_rows.size, d))
+    dK = np.zeros((k_rows.size, d))
+    dV = np.zeros((k_rows.size, d))
+    n_keys = min(L, N)
+    # every query row contributes to a key's gradient; a query row's own
+    # gradient needs only that row
+    visit = np.arange(N) if k_rows.size else np.unique(q_rows)
+    for c0 in range(0, visit.size, chunk):
+        r = visit[c0:c0 + chunk]
+        # keys a row of this chunk can see: j < L, and j <= i when causal
+        kmax = min(n_keys, int(r.max()) + 1) if causal else n_keys
+        if kmax == 0:
+            continue
+        S = s64 * (Qf[r] @ Kf[:kmax].T)
+        ok = allowed_mask(r, kmax, L, causal)
+        P, _ = _softmax_rows(S, ok)
+        dP = dOf[r] @ Vf[:kmax].T
+        Dr = (P * dP).sum(axis=1, keepdims=True)
+        dS = P * (dP - Dr)
+        pos = {int(i): n for n, i in enumerate(r)}
+        for n, i in enumerate(q_rows):
+            if int(i) in pos:
+                dQ[n] = s64 * (dS[pos[int(i)]] @ Kf[:kmax])
+        ksel = np.nonzero(k_rows < kmax)[0]
+        if ksel.size:
+            cols = k_rows[ksel]
+            dV[ksel] += P[:, cols].T @ dOf[r]
+            dK[ksel] += s64 * (dS[:, cols].T @ Qf[r])
     return dQ, dK, dV

@@ -454,3 +454,57 @@ def test_backward_invariants():
     np.testing.assert_allclose(dq, dq2, atol=1e-12)
     np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
     np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)   # sum_j dK_j = s sum_i (sum_j dS_ij) q_i = 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("padded", [False, True])
+def test_sampled_backward_matches_finite_differences(causal, padded):
+    """The chunked, sampled backward against central differences of the forward
+    oracle's loss, with chunks smaller than N so rows and keys span chunks."""
+    B, H, N, d = 2, 2, 7, 3
+    seed = 9500 + 2 * causal + padded
+    q, k, v, do = (_rand((B, H, N, d), seed + t, sd=0.9) for t in range(4))
+    kv_len = np.array([5, 7]) if padded else None
+    scale, h = 0.7, 1e-6
+    b, hh = 1 if not padded else 0, 1
+    q_rows, k_rows = np.array([6, 0, 3]), np.array([2, 6, 4, 0])
+    dq, dk, dv = oracle.attention_bwd_sampled_fp64(q, k, v, do, scale, causal, kv_len, "f64",
+                                                   b, hh, q_rows, k_rows, chunk=3)
+    for name, rows_sel, g in (("q", q_rows, dq), ("k", k_rows, dk), ("v", k_rows, dv)):
+        for n, i in enumerate(rows_sel):
+            for c in range(d):
+                args = {"q": q, "k": k, "v": v}
+                base = args[name]
+                xp = base.copy(); xp[b, hh, i, c] += h
+                xm = base.copy(); xm[b, hh, i, c] -= h
+                args[name] = xp
+                lp = _loss(args["q"], args["k"], args["v"], do, scale, causal, kv_len)
+                args[name] = xm
+                lm = _loss(args["q"], args["k"], args["v"], do, scale, causal, kv_len)
+                assert abs(g[n, c] - (lp - lm) / (2 * h)) <= 2e-8, (name, i, c)
+
+
+def test_sampled_backward_equals_dense():
+    B, H, N, d = 2, 2, 300, 16
+    q, k, v, do = (_rand((B, H, N, d), 9600 + t) for t in range(4))
+    kv_len = np.array([300, 123])
+    for causal in (False, True):
+        dense = oracle.attention_bwd_fp64(q, k, v, do, 0.25, causal, kv_len, kind="f64")
+        for b in range(B):
+            rows = np.array([0, 1, 64, 122, 123, 299])
+            got = oracle.attention_bwd_sampled_fp64(q, k, v, do, 0.25, causal, kv_len, "f64",
+                                                    b, 1, rows, rows, chunk=64)
+            for g, full in zip(got, dense):
+                np.testing.assert_allclose(g, full[b, 1, rows], rtol=0, atol=1e-12)
+
+
+def test_sampled_backward_query_rows_only():
+    B, H, N, d = 1, 1, 200, 8
+    q, k, v, do = (_rand((B, H, N, d), 9700 + t) for t in range(4))
+    rows = np.array([199, 3, 77, 0, 3])
+    for causal in (False, True):
+        dense = oracle.attention_bwd_fp64(q, k, v, do, 0.3, causal, None, kind="f64")
+        dq, dk, dv = oracle.attention_bwd_sampled_fp64(q, k, v, do, 0.3, causal, None, "f64",
+                                                       0, 0, rows, [], chunk=2)
+        np.testing.assert_allclose(dq, dense[0][0, 0, rows], rtol=0, atol=1e-12)
+        assert dk.shape == (0, d) and dv.shape == (0, d)
