@@ -13,7 +13,13 @@ counter summary is committed under profiles/, and the fp64 CPU oracle timed on
 a bounded row sample on the host cores (which also checks those rows).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --mode bwd [--workload NAME]   # the backward (bf16 workloads)
   python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
+
+In --mode bwd one step is one attn_bwd call (its three kernels) from the
+forward's O and log-sum-exp, which are computed before the timed region; the
+throughput counts 10*d FLOPs per visible pair (the five products S, dP, dV, dK,
+dQ of the backward, each 2*d per pair).
 """
 
 from __future__ import annotations
@@ -132,6 +138,76 @@ def cpu_baseline(w, q, k, v, kv_len, out, budget_s: float):
     }
 
 
+def bench_bwd(w, args) -> int:
+    import torch
+
+    from exact_long_sequence_amd import attnio
+    from exact_long_sequence_amd.inputs import workload_inputs
+    if w.dtype != "bf16":
+        print("the backward is bf16 only", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    q, k, v, kv_len = workload_inputs(w)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 7919)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    del q, k, v, do
+    kvd = None if kv_len is None else kv_len.to(dev)
+    o, lse = attnio.attn_fwd_lse(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(attnio.attn_bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    model = attnio.attn_io_model(w.B, w.H, w.N, w.d, 2, w.causal,
+                                 None if kv_len is None else kv_len.tolist())
+
+    def step():
+        attnio.attn_bwd(qd, kd, vd, o, dod, lse, causal=w.causal, kv_len=kvd, scale=w.scale,
+                        dq=dq, dk=dk, dv=dv, workspace=ws)
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    flops = 10.0 * w.d * model["pairs"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    # compulsory bytes: Q, K, V, O, dO read and dQ, dK, dV written once, plus
+    # the per-row log-sum-exp
+    t_min = 8.0 * w.B * w.H * w.N * w.d * 2 + 4.0 * w.B * w.H * w.N
+    result = {
+        "metric": "attention bwd TFLOP/s (algorithmic 10*d per visible query-key pair)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO)",
+        "config": {**w.describe(), "pass": "backward"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+        },
+        "io": {"t_min_bytes": t_min, "t_min_rate_GBs": t_min / (ms * 1e-3) / 1e9},
+        "executed_flops_per_pair": 14 * w.d,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +217,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
+    ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -159,6 +236,8 @@ def main() -> int:
     from exact_long_sequence_amd.inputs import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
+    if args.mode == "bwd":
+        return bench_bwd(w, args)
     dev = torch.device("cuda:0")
     q, k, v, kv_len = workload_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)

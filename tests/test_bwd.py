@@ -54,6 +54,7 @@ def _check_grad(got, want, label):
     ref_max = float(np.abs(want).max(initial=0.0))
     ref_mean = float(np.abs(want).mean()) if want.size else 0.0
     mx, mn = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    _log(f"  {label}: max_err/max|ref|={mx / max(ref_max, 1e-30):.2e} mean_err/mean|ref|={mn / max(ref_mean, 1e-30):.2e}")
     assert mx <= TOL_MAX * ref_max + 1e-6, f"{label}: max_err={mx:.3e} max|ref|={ref_max:.3e}"
     assert mn <= TOL_MEAN * ref_mean + 1e-7, f"{label}: mean_err={mn:.3e} mean|ref|={ref_mean:.3e}"
 
@@ -136,3 +137,65 @@ def test_bwd_reuses_caller_buffers():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# Full-size workloads: the backward runs at the workload's shape in the launch
+# configuration the benchmark times, and the oracle computes sampled gradient
+# rows of a few heads one by one (query rows anywhere; key rows anywhere when
+# the oracle can visit every query row of the head in seconds, else the last
+# 4096 keys, which under the causal mask only the last 4096 rows reach).
+FULL = {
+    "bf16_h16_n8k_d128": {"heads": [(0, 0), (0, 15)], "late_keys": False},
+    "bf16_causal_h32_n32k_d128": {"heads": [(0, 31)], "late_keys": False},
+    "bf16_causal_h8_n128k_d64": {"heads": [(0, 0), (0, 7)], "late_keys": True},
+    "bf16_padded_b4_h32_n16k_d128_q8": {"heads": "min_max_len", "late_keys": False},
+}
+
+
+def _pick(rng, lo, hi, n, must):
+    lo, hi = max(lo, 0), max(hi, 0)
+    base = rng.choice(np.arange(lo, hi), size=min(n, hi - lo), replace=False) if hi > lo else []
+    extra = [i for i in must if lo <= i < hi]
+    return np.unique(np.concatenate([np.asarray(base, dtype=np.int64), np.asarray(extra, dtype=np.int64)]))
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_bwd_full_size_sampled(name):
+    from exact_long_sequence_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS[name]
+    spec = FULL[name]
+    _log(f"bwd full {name}: inputs")
+    q, k, v, kv = workload_inputs(w)
+    do = _dout(q.shape, w.seed)
+    kvd = None if kv is None else kv.to(DEV)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    _log(f"bwd full {name}: forward + backward on the GPU")
+    o, lse = attnio.attn_fwd_lse(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale)
+    dq, dk, dv = attnio.attn_bwd(qd, kd, vd, o, dod, lse, causal=w.causal, kv_len=kvd, scale=w.scale)
+    torch.cuda.synchronize()
+    del qd, kd, vd, o, lse
+    Ls = [w.N] * w.B if kv is None else [int(x) for x in kv]
+    heads = spec["heads"]
+    if heads == "min_max_len":
+        heads = [(int(np.argmin(Ls)), 0), (int(np.argmax(Ls)), w.H - 1)]
+    views = [oracle_view(t) for t in (q, k, v, do)]
+    kv_np = None if kv is None else kv.numpy()
+    for (b, h) in heads:
+        L = Ls[b]
+        rng = np.random.default_rng(w.seed + 31 * b + h)
+        edge = [0, 1, 63, 64, 127, 128, w.N - 2, w.N - 1, L - 1, L]
+        q_rows = _pick(rng, 0, w.N, 24, edge)
+        k_lo = w.N - 4096 if spec["late_keys"] else 0
+        k_rows = _pick(rng, k_lo, w.N, 24, edge)
+        _log(f"bwd full {name}: oracle head (b={b}, h={h}) L={L} on {q_rows.size} query rows, "
+             f"{k_rows.size} key rows from {k_lo}")
+        want = oracle.attention_bwd_sampled_fp64(*views, w.scale, w.causal, kv_np, "bf16", b, h,
+                                                 q_rows, k_rows)
+        qi = torch.as_tensor(q_rows, device=DEV)
+        ki = torch.as_tensor(k_rows, device=DEV)
+        got = (dq[b, h].index_select(0, qi), dk[b, h].index_select(0, ki), dv[b, h].index_select(0, ki))
+        for gname, g, ref in zip(("dQ", "dK", "dV"), got, want):
+            _check_grad(g, ref, f"{name} {gname} head ({b},{h})")
+        if L < w.N:
+            assert torch.count_nonzero(dk[b, h, L:]).item() == 0
+            assert torch.count_nonzero(dv[b, h, L:]).item() == 0

@@ -508,3 +508,18 @@ def test_sampled_backward_query_rows_only():
                                                        0, 0, rows, [], chunk=2)
         np.testing.assert_allclose(dq, dense[0][0, 0, rows], rtol=0, atol=1e-12)
         assert dk.shape == (0, d) and dv.shape == (0, d)
+
+
+def test_sampled_backward_late_keys_causal():
+    # under the causal mask only rows i >= j reach key j: selecting late keys
+    # visits only late rows, with the same result as the dense backward
+    B, H, N, d = 1, 1, 260, 8
+    q, k, v, do = (_rand((B, H, N, d), 9800 + t) for t in range(4))
+    dense = oracle.attention_bwd_fp64(q, k, v, do, 0.4, True, None, kind="f64")
+    keys = np.array([259, 200, 230])
+    rows = np.array([5, 250])
+    got = oracle.attention_bwd_sampled_fp64(q, k, v, do, 0.4, True, None, "f64", 0, 0, rows, keys,
+                                            chunk=16)
+    np.testing.assert_allclose(got[0], dense[0][0, 0, rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[1], dense[1][0, 0, keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[2], dense[2][0, 0, keys], rtol=0, atol=1e-12)
