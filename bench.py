@@ -14,6 +14,7 @@ a bounded row sample on the host cores (which also checks those rows).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --mode bwd [--workload NAME]   # the backward (bf16 workloads)
+  python bench.py --mode unfused [--workload NAME] [--heads-per-pass G]
   python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
 
 In --mode bwd one step is one attn_bwd call (its three kernels) from the
@@ -208,6 +209,89 @@ def bench_bwd(w, args) -> int:
     return 0
 
 
+def bench_unfused(w, args) -> int:
+    """The operator-centric baseline: three kernels per group of heads with the
+    N x N scores and probabilities in HBM.  Same algorithmic FLOPs as the fused
+    forward, so the two TFLOP/s figures compare directly; the fused kernel is
+    timed in the same process for the ratio."""
+    import torch
+
+    from exact_long_sequence_amd import attnio
+    from exact_long_sequence_amd.inputs import workload_inputs
+    if w.dtype != "bf16":
+        print("the unfused baseline is bf16 only", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    q, k, v, kv_len = workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    kvd = None if kv_len is None else kv_len.to(dev)
+    out = torch.empty_like(qd)
+    hp = max(1, min(args.heads_per_pass, w.B * w.H))
+    ws = torch.empty(hp * attnio.attn_fwd_unfused_workspace_bytes(w.N), dtype=torch.uint8, device=dev)
+    model = attnio.attn_io_model(w.B, w.H, w.N, w.d, 2, w.causal,
+                                 None if kv_len is None else kv_len.tolist())
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    ms = timed(lambda: attnio.attn_fwd_unfused(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale,
+                                               out=out, workspace=ws), args.steps, args.warmup)
+    ms_fused = timed(lambda: attnio.attn_fwd(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale,
+                                             out=out), max(args.steps, 5), 2)
+    tflops = model["flops"] / (ms * 1e-3) / 1e12
+    traffic = None
+    summary = os.path.join(ROOT, "profiles", "attn_fwd_unfused_bf16_causal_b1_h32_n32k_d128_trace_counters.md")
+    if w.name == "bf16_causal_h32_n32k_d128" and hp == 8 and os.path.exists(summary):
+        text = open(summary).read()
+        src = os.path.join(ROOT, "exact_long_sequence_amd", "csrc", "attn_unfused_bf16.hip")
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+        m_b = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", text)
+        if m_sha and m_b and m_sha.group(1) == digest:
+            traffic = float(m_b.group(1))
+    nn = float(w.N) * w.N * w.B * w.H
+    # intermediates written and read once each: S (fp32) and P (bf16)
+    inter = nn * (4 + 4 + 2 + 2)
+    result = {
+        "metric": "attention fwd TFLOP/s, operator-centric baseline (algorithmic 4*d per visible pair)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": {**w.describe(), "pass": "forward, unfused", "heads_per_pass": hp},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": (model["t_min"] + inter) / (ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": (model["t_min"] + inter) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "io": {"t_min_bytes": model["t_min"], "intermediate_bytes_min": inter},
+        "fused_ms_per_step": ms_fused,
+        "fused_speedup": ms / ms_fused,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,7 +301,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
-    ap.add_argument("--mode", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused"), default="fwd")
+    ap.add_argument("--heads-per-pass", type=int, default=8,
+                    help="--mode unfused: heads whose N x N intermediates share the workspace")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -238,6 +324,8 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     if args.mode == "bwd":
         return bench_bwd(w, args)
+    if args.mode == "unfused":
+        return bench_unfused(w, args)
     dev = torch.device("cuda:0")
     q, k, v, kv_len = workload_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)

@@ -21,7 +21,8 @@ _lib = None
 ATTN_OK = 0
 
 __all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_strerror", "attn_version", "attn_query_tiling",
+           "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
+           "attn_strerror", "attn_version", "attn_query_tiling",
            "attn_io_model", "library_path", "load_library"]
 
 
@@ -51,6 +52,10 @@ def load_library() -> ctypes.CDLL:
     lib.attn_bwd.restype = i32
     lib.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_unfused.argtypes = [vp] * 5 + [ctypes.c_size_t, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_fwd_unfused.restype = i32
+    lib.attn_fwd_unfused_workspace_bytes.argtypes = [i32]
+    lib.attn_fwd_unfused_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -242,3 +247,43 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_bwd: {attn_strerror(rc)} (code {rc})")
     return tuple(grads)
+
+
+def attn_fwd_unfused_workspace_bytes(N: int) -> int:
+    """Workspace bytes one head of the unfused forward needs (6 N^2)."""
+    return int(load_library().attn_fwd_unfused_workspace_bytes(int(N)))
+
+
+def attn_fwd_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                     kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     heads_per_pass: int = 1) -> torch.Tensor:
+    """Operator-centric bf16 forward (scores, softmax, P V as three kernels with
+    the N x N intermediates in a workspace).  Same contract as attn_fwd.
+
+    workspace: optional uint8 device tensor; by default one of
+    heads_per_pass * attn_fwd_unfused_workspace_bytes(N) bytes is allocated."""
+    lib = load_library()
+    _check(q, k, v, torch.bfloat16)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor like q")
+    if workspace is None:
+        per_head = attn_fwd_unfused_workspace_bytes(N)
+        workspace = torch.empty(per_head * max(1, int(heads_per_pass)), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device buffer")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    kv_len, kv_ptr = _kv_len_ptr(kv_len, B, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  workspace.data_ptr(), ws_bytes, B, H, N, d, float(scale),
+                                  int(bool(causal)), kv_ptr, stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_unfused: {attn_strerror(rc)} (code {rc})")
+    return out

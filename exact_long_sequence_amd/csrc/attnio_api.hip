@@ -171,6 +171,34 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   return ATTN_OK;
 }
 
+size_t attn_fwd_unfused_workspace_bytes(int N) {
+  if (N < 1) return 0;
+  return attnio::unfused_head_bytes(N);
+}
+
+int attn_fwd_unfused(const void* Q, const void* K, const void* V, void* O, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                     const int32_t* kv_len, void* stream) {
+  if (!workspace) return ATTN_E_NULL;
+  int rc = validate(Q, K, V, O, B, H, N, d, scale, 2);
+  if (rc != ATTN_OK) return rc;
+  if ((uintptr_t)workspace & 255u) return ATTN_E_ALIGN;
+  if (workspace_bytes < attnio::unfused_head_bytes(N)) return ATTN_E_ARG;
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const void* ins[4] = {Q, K, V, O};
+  for (int j = 0; j < 4; ++j)
+    if (ranges_overlap(workspace, workspace_bytes, ins[j], tb)) return ATTN_E_ALIAS;
+  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  attnio::UnfusedArgs a{Q, K, V, O, workspace, workspace_bytes, kv_len, B, H, N, d, scale,
+                        causal ? 1 : 0};
+  const hipError_t e = attnio::launch_unfused_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (log_enabled()) fprintf(stderr, "[attnio] unfused launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
 const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "success";

@@ -48,7 +48,24 @@ struct BwdArgs {
   int causal;
 };
 
+// Unfused (operator-centric) forward: S and P of up to ws_bytes / unfused_head_bytes(N)
+// heads at a time live in the caller's workspace.
+struct UnfusedArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  void* ws;
+  size_t ws_bytes;
+  const int32_t* kv_len;
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
 bool bf16_tiling(int d, int causal, Tiling* t);
+size_t unfused_head_bytes(int N);
+hipError_t launch_unfused_bf16(const UnfusedArgs& a, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

@@ -116,6 +116,25 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
  * only; 0 for non-positive sizes). */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
+/* Operator-centric (unfused) bf16 forward, the baseline the fused kernel is
+ * measured against ("From Attention Graph to FlashAttention - A Memory-Centric
+ * Compilation Approach in AICF", section 2: one kernel per operator, each
+ * result handed to the next operator through memory).  Same inputs, output and
+ * conventions as attn_fwd; three kernels per group of heads: scores
+ * S = scale Q K^T for all N x N pairs written in fp32, a row softmax that
+ * applies the causal / padding mask and writes P in bf16 (normalised in fp32,
+ * rounded once), and O = P V over all N keys.  The N x N intermediates live in
+ * the caller's workspace: attn_fwd_unfused_workspace_bytes(N) bytes per head
+ * (6 N^2), at least one head's worth, 256-byte aligned, not overlapping any
+ * tensor; the call processes floor(workspace_bytes / that) heads at a time.
+ * Returns ATTN_E_ARG if the workspace holds less than one head. */
+int attn_fwd_unfused(const void* Q, const void* K, const void* V, void* O, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                     int causal, const int32_t* kv_len, void* stream);
+
+/* Workspace bytes one head of attn_fwd_unfused needs (host only; 0 for N < 1). */
+size_t attn_fwd_unfused_workspace_bytes(int N);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_strerror(int code);
 

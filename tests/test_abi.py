@@ -31,8 +31,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
-            "attn_bwd_workspace_bytes", "attn_strerror", "attn_version", "attn_query_tiling",
-            "attn_io_model"} <= names
+            "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
+            "attn_strerror", "attn_version", "attn_query_tiling", "attn_io_model"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -107,6 +107,26 @@ def test_bwd_entry_argument_errors(lib):
     assert call(dV=base["LSE"] + 16) == -7
     assert call(ws=base["dQ"] + 512) == -7           # workspace overlaps an output
     assert call(dK=base["dV"] + 1024) == -7          # outputs overlap each other
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert call() == -6
+
+
+def test_unfused_entry_argument_errors(lib):
+    assert attnio.attn_fwd_unfused_workspace_bytes(1000) == 6 * 1000 * 1000
+    assert attnio.attn_fwd_unfused_workspace_bytes(0) == 0
+    ws = 0x10000000
+    need = 6 * 16 * 16
+
+    def call(q=0x1000, o=0x6000000, w=ws, nbytes=need, d=64):
+        return lib.attn_fwd_unfused(q, 0x2000000, 0x4000000, o, w, nbytes, 1, 1, 16, d,
+                                    ctypes.c_float(0.125), 0, None, None)
+    assert call(w=None) == -1
+    assert call(q=None) == -1
+    assert call(d=96) == -2
+    assert call(w=ws + 16) == -4                   # workspace must be 256-byte aligned
+    assert call(nbytes=need - 1) == -8             # less than one head
+    assert call(w=0x6000000 - 256) == -7           # workspace overlaps O
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         assert call() == -6
