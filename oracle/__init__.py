@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for exact attention (forward, lse, backward) -- test infrastructure only.
+"""fp64 CPU oracle for exact attention (forward, lse, backward) and the streaming row
+operators (softmax, LayerNorm) -- test infrastructure only.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP path.
@@ -17,3 +18,4 @@ from .attention import (  # noqa: F401
     effective_kv_len,
     to_fp64,
 )
+from .rows import layernorm_rows_fp64, softmax_rows_fp64  # noqa: F401

@@ -298,8 +298,10 @@ def attention_bwd_sampled_fp64(q, k, v, do, scale: float, causal: bool, kv_len, 
     softmax, D_i = rowsum(P * dP) and dS need only that row, so each chunk
     completes its rows; the key-side gradients are sums over query rows,
         dV_j = sum_i P_ij dO_i,    dK_j = s sum_i dS_ij Q_i,
-    accumulated chunk by chunk for the selected keys j only.  With no key rows
-    selected, only the selected query rows are visited."""
+    accumulated chunk by chunk for the selected keys j only.  Rows that
+    contribute nothing to what was asked for (rows before the first selected
+    key under the causal mask, unselected rows when no key is selected) are
+    never visited."""
     qa, ka, va, da = (np.asarray(t) for t in (q, k, v, do))
     B, H, N, d = qa.shape
     L = int(effective_kv_len(kv_len, B, N)[b])
@@ -311,9 +313,12 @@ def attention_bwd_sampled_fp64(q, k, v, do, scale: float, causal: bool, kv_len, 
     dK = np.zeros((k_rows.size, d))
     dV = np.zeros((k_rows.size, d))
     n_keys = min(L, N)
-    # every query row contributes to a key's gradient; a query row's own
-    # gradient needs only that row
-    visit = np.arange(N) if k_rows.size else np.unique(q_rows)
+    # a query row's own gradient needs only that row; key j's gradients need
+    # every row that sees key j: all rows, or under the causal mask rows i >= j
+    visit = np.unique(q_rows)
+    if k_rows.size:
+        first = int(k_rows.min()) if causal else 0
+        visit = np.union1d(visit, np.arange(first, N))
     for c0 in range(0, visit.size, chunk):
         r = visit[c0:c0 + chunk]
         # keys a row of this chunk can see: j < L, and j <= i when causal
