@@ -15,6 +15,7 @@ a bounded row sample on the host cores (which also checks those rows).
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --mode bwd [--workload NAME]   # the backward (bf16 workloads)
   python bench.py --mode unfused [--workload NAME] [--heads-per-pass G]
+  python bench.py --mode rows [--workload softmax_r32k_n32k|layernorm_r128k_n8k]
   python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
 
 In --mode bwd one step is one attn_bwd call (its three kernels) from the
@@ -292,6 +293,94 @@ def bench_unfused(w, args) -> int:
     return 0
 
 
+def bench_rows(args) -> int:
+    """A streaming row operator (softmax or LayerNorm) over a bf16 [R, N]
+    matrix: HBM-bound, so the roofline is HBM bandwidth and the figure is the
+    compulsory bytes (read x once, write y once, plus gamma and beta) per
+    second."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_long_sequence_amd import attnio
+    from exact_long_sequence_amd.inputs import ROW_WORKLOADS, oracle_view, row_workload_inputs
+    name = args.workload if args.workload in ROW_WORKLOADS else "softmax_r32k_n32k"
+    w = ROW_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    x, gamma, beta = row_workload_inputs(w)
+    xd = x.to(dev)
+    y = torch.empty_like(xd)
+    gd = None if gamma is None else gamma.to(dev)
+    bd = None if beta is None else beta.to(dev)
+    if w.op == "softmax":
+        fn = lambda: attnio.stream_softmax(xd, w.param, out=y)  # noqa: E731
+    else:
+        fn = lambda: attnio.stream_layernorm(xd, gd, bd, eps=w.param, out=y)  # noqa: E731
+    for _ in range(args.warmup):
+        fn()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    t_min = 2.0 * w.R * w.N * 2 + (0 if gamma is None else 2 * w.N * 2)
+    gbs = t_min / (ms * 1e-3) / 1e9
+    # a plain device copy of the same bytes, for the achievable bandwidth
+    for _ in range(2):
+        y.copy_(xd)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        y.copy_(xd)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * w.R * w.N * 2 / (start.elapsed_time(stop) / args.steps * 1e-3) / 1e9
+    result = {
+        "metric": f"stream_{w.op} GB/s (compulsory bytes: x read once, y written once)",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rows)",
+        "config": w.describe(),
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "cached_in_registers": attnio.stream_rows_cached(w.N),
+        "plain_copy_GBs": copy_gbs,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on a bounded sample of rows, timed on the host cores
+        rng = np.random.default_rng(w.seed + 5)
+        rows = rng.permutation(w.R)
+        t0 = time.perf_counter()
+        done = 0
+        while done < w.R and time.perf_counter() - t0 < args.cpu_budget:
+            r = rows[done:done + 64]
+            xs = oracle_view(x[torch.as_tensor(r)])
+            if w.op == "softmax":
+                oracle.softmax_rows_fp64(xs, w.param)
+            else:
+                oracle.layernorm_rows_fp64(xs, oracle_view(gamma), oracle_view(beta), eps=w.param)
+            done += r.size
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": 2.0 * done * w.N * 2 / dt / 1e9, "unit": "GB/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{done} seeded rows of {w.name}, fp64 numpy, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,7 +390,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
-    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused"), default="fwd")
+    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused", "rows"), default="fwd")
     ap.add_argument("--heads-per-pass", type=int, default=8,
                     help="--mode unfused: heads whose N x N intermediates share the workspace")
     args = ap.parse_args()
@@ -321,6 +410,8 @@ def main() -> int:
     from exact_long_sequence_amd import attnio
     from exact_long_sequence_amd.inputs import WORKLOADS, workload_inputs
 
+    if args.mode == "rows":
+        return bench_rows(args)
     w = WORKLOADS[args.workload]
     if args.mode == "bwd":
         return bench_bwd(w, args)

@@ -22,7 +22,7 @@ ATTN_OK = 0
 
 __all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
-           "attn_strerror", "attn_version", "attn_query_tiling",
+           "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_strerror", "attn_version", "attn_query_tiling",
            "attn_io_model", "library_path", "load_library"]
 
 
@@ -56,6 +56,12 @@ def load_library() -> ctypes.CDLL:
     lib.attn_fwd_unfused.restype = i32
     lib.attn_fwd_unfused_workspace_bytes.argtypes = [i32]
     lib.attn_fwd_unfused_workspace_bytes.restype = ctypes.c_size_t
+    lib.stream_softmax.argtypes = [vp, vp, i32, i32, f32, vp]
+    lib.stream_softmax.restype = i32
+    lib.stream_layernorm.argtypes = [vp, vp, vp, vp, i32, i32, f32, vp]
+    lib.stream_layernorm.restype = i32
+    lib.stream_rows_cached.argtypes = [i32]
+    lib.stream_rows_cached.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -286,4 +292,58 @@ def attn_fwd_unfused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
                                   int(bool(causal)), kv_ptr, stream)
     if rc != ATTN_OK:
         raise RuntimeError(f"attn_fwd_unfused: {attn_strerror(rc)} (code {rc})")
+    return out
+
+
+def stream_rows_cached(N: int) -> bool:
+    """True if a row of N elements is held in registers (read from HBM once)."""
+    return bool(load_library().stream_rows_cached(int(N)))
+
+
+def _check_rows(x, out):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a bf16 tensor on a GPU device")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [R, N] tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous bf16 tensor like x")
+    return out
+
+
+def stream_softmax(x: torch.Tensor, scale: float = 1.0, *, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row softmax of scale * x for a bf16 [R, N] device tensor (out may be x)."""
+    lib = load_library()
+    out = _check_rows(x, out)
+    R, N = x.shape
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.stream_softmax(x.data_ptr(), out.data_ptr(), R, N, float(scale), stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"stream_softmax: {attn_strerror(rc)} (code {rc})")
+    return out
+
+
+def stream_layernorm(x: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                     beta: Optional[torch.Tensor] = None, eps: float = 1e-5, *,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row LayerNorm of a bf16 [R, N] device tensor; gamma / beta bf16 [N] or None."""
+    lib = load_library()
+    out = _check_rows(x, out)
+    R, N = x.shape
+    ptrs = []
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if (not isinstance(t, torch.Tensor) or t.device != x.device or t.dtype != torch.bfloat16
+                or t.numel() != N or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of N={N} elements on x's device")
+        ptrs.append(t.data_ptr())
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        rc = lib.stream_layernorm(x.data_ptr(), ptrs[0], ptrs[1], out.data_ptr(), R, N, float(eps), stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"stream_layernorm: {attn_strerror(rc)} (code {rc})")
     return out

@@ -3,6 +3,7 @@
 // contract of every entry point.
 
 #include <hip/hip_runtime.h>
+#include <cmath>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -198,6 +199,41 @@ int attn_fwd_unfused(const void* Q, const void* K, const void* V, void* O, void*
   }
   return ATTN_OK;
 }
+
+namespace {
+int run_rows(const void* X, const void* gamma, const void* beta, void* Y, int R, int N, int op,
+             float param, void* stream) {
+  if (!X || !Y) return ATTN_E_NULL;
+  if (R < 1 || N < 1 || (long long)R * N >= (1LL << 40)) return ATTN_E_SHAPE;
+  if (((uintptr_t)X | (uintptr_t)Y | (uintptr_t)gamma | (uintptr_t)beta) & 15u) return ATTN_E_ALIGN;
+  if (!std::isfinite(param) || !(param > 0.f)) return ATTN_E_ARG;
+  const size_t xb = (size_t)R * N * 2, vb = (size_t)N * 2;
+  // Y may be X itself (each element is read before it is written, by the same
+  // thread); any other overlap is rejected, as is Y overlapping gamma or beta
+  if (X != Y && ranges_overlap(X, xb, Y, xb)) return ATTN_E_ALIAS;
+  if ((gamma && ranges_overlap(gamma, vb, Y, xb)) || (beta && ranges_overlap(beta, vb, Y, xb)))
+    return ATTN_E_ALIAS;
+  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  attnio::RowArgs a{X, Y, gamma, beta, R, N, op, param};
+  const hipError_t e = attnio::launch_stream_rows(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (log_enabled()) fprintf(stderr, "[attnio] row kernel launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+}  // namespace
+
+int stream_softmax(const void* X, void* Y, int R, int N, float scale, void* stream) {
+  return run_rows(X, nullptr, nullptr, Y, R, N, 0, scale, stream);
+}
+
+int stream_layernorm(const void* X, const void* gamma, const void* beta, void* Y, int R, int N,
+                     float eps, void* stream) {
+  return run_rows(X, gamma, beta, Y, R, N, 1, eps, stream);
+}
+
+int stream_rows_cached(int N) { return N < 1 ? 0 : attnio::rows_cached_sweeps(N) > 0; }
 
 const char* attn_strerror(int code) {
   switch (code) {

@@ -63,7 +63,21 @@ struct UnfusedArgs {
   int causal;
 };
 
+// Streaming row operators on a bf16 [R, N] matrix (op 0: softmax with
+// param = scale; op 1: LayerNorm with param = eps, optional gamma / beta).
+struct RowArgs {
+  const void* x;
+  void* y;
+  const void* gamma;
+  const void* beta;
+  int R, N;
+  int op;
+  float param;
+};
+
 bool bf16_tiling(int d, int causal, Tiling* t);
+int rows_cached_sweeps(int N);
+hipError_t launch_stream_rows(const RowArgs& a, hipStream_t stream);
 size_t unfused_head_bytes(int N);
 hipError_t launch_unfused_bf16(const UnfusedArgs& a, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int H, int N);

@@ -22,7 +22,8 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "oracle_view", "sample_rows"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "oracle_view", "sample_rows", "RowWorkload",
+           "ROW_WORKLOADS", "row_workload_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -127,3 +128,41 @@ def sample_rows(B: int, H: int, N: int, n_sample: int, seed: int, boundary_bm: i
                     extra.append((b * H) * N + i)
     rows = np.unique(np.concatenate([picked, np.asarray(extra, dtype=np.int64)]))
     return rows.astype(np.int64)
+
+
+@dataclasses.dataclass(frozen=True)
+class RowWorkload:
+    """A streaming row operator over a bf16 [R, N] matrix."""
+    name: str
+    op: str          # "softmax" or "layernorm"
+    R: int
+    N: int
+    param: float     # softmax scale or LayerNorm eps
+    seed: int
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "op": self.op, "R": self.R, "N": self.N,
+                "param": self.param, "seed": self.seed, "dtype": "bf16"}
+
+
+# Row workloads at the attention path's scale: the full score matrix of one
+# 32768-row head, and the 131072-token activations of a d=64 x 128-head model
+# (hidden size 8192).  Recipe: a seeded CPU torch.Generator draws x as fp32
+# N(0, 1) [R, N]; for LayerNorm it then draws gamma = 1 + 0.1 N(0, 1) and
+# beta = 0.1 N(0, 1) of length N; everything is rounded to bf16.
+ROW_WORKLOADS = {
+    "softmax_r32k_n32k": RowWorkload("softmax_r32k_n32k", "softmax", 32768, 32768, 1.0, 1101),
+    "layernorm_r128k_n8k": RowWorkload("layernorm_r128k_n8k", "layernorm", 131072, 8192, 1e-5, 1102),
+}
+
+
+def row_workload_inputs(w: RowWorkload):
+    """(x, gamma, beta) on the CPU; gamma and beta are None for softmax."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(w.seed))
+    x = torch.randn((w.R, w.N), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    if w.op == "softmax":
+        return x, None, None
+    gamma = (1.0 + 0.1 * torch.randn((w.N,), generator=g, dtype=torch.float32)).to(torch.bfloat16)
+    beta = (0.1 * torch.randn((w.N,), generator=g, dtype=torch.float32)).to(torch.bfloat16)
+    return x, gamma, beta

@@ -135,6 +135,31 @@ int attn_fwd_unfused(const void* Q, const void* K, const void* V, void* O, void*
 /* Workspace bytes one head of attn_fwd_unfused needs (host only; 0 for N < 1). */
 size_t attn_fwd_unfused_workspace_bytes(int N);
 
+/* Streaming row operators ("From Attention Graph to FlashAttention - A
+ * Memory-Centric Compilation Approach in AICF", closing outlook: streaming
+ * softmax and streaming LayerNorm as further memory-centric operators).
+ * X and Y are contiguous row-major bf16 [R, N] device matrices (16-byte
+ * aligned); each row is reduced and mapped on its own, in fp32, and written
+ * rounded to bf16 once.  A row that fits one workgroup's registers
+ * (stream_rows_cached(N) == 1: N % 8 == 0 and N <= 65536) is read from HBM
+ * once; longer rows are read twice.  Y may be X itself (in place); any other
+ * overlap is ATTN_E_ALIAS.  R, N >= 1 and R * N < 2^40.  Enqueued on
+ * `stream`; nothing allocated, nothing synchronised.
+ *
+ * stream_softmax:   Y[r, j] = exp(scale X[r, j]) / sum_k exp(scale X[r, k]);
+ *                   -inf entries get 0 and a row of all -inf gives zeros.
+ *                   scale must be finite and > 0 (else ATTN_E_ARG).
+ * stream_layernorm: Y[r, j] = (X[r, j] - mean_r) / sqrt(var_r + eps) * gamma[j]
+ *                   + beta[j], with the biased variance; gamma and beta are
+ *                   bf16 [N] device vectors (16-byte aligned) or NULL (1 and
+ *                   0).  eps must be finite and > 0 (else ATTN_E_ARG). */
+int stream_softmax(const void* X, void* Y, int R, int N, float scale, void* stream);
+int stream_layernorm(const void* X, const void* gamma, const void* beta, void* Y, int R, int N,
+                     float eps, void* stream);
+
+/* 1 if a row of N elements is held in registers (one HBM read), else 0. Host only. */
+int stream_rows_cached(int N);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_strerror(int code);
 

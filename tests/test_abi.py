@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "attnio.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:attn|stream)_\w+)\s*\(", text, flags=re.M)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
-            "attn_strerror", "attn_version", "attn_query_tiling", "attn_io_model"} <= names
+            "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_strerror", "attn_version",
+            "attn_query_tiling", "attn_io_model"} <= names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -130,6 +131,30 @@ def test_unfused_entry_argument_errors(lib):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         assert call() == -6
+
+
+def test_stream_rows_argument_errors(lib):
+    X, Y, G = 0x100000, 0x900000, 0x2000000
+
+    def sm(x=X, y=Y, R=4, N=1024, scale=1.0):
+        return lib.stream_softmax(x, y, R, N, ctypes.c_float(scale), None)
+
+    def ln(x=X, g=G, b=None, y=Y, R=4, N=1024, eps=1e-5):
+        return lib.stream_layernorm(x, g, b, y, R, N, ctypes.c_float(eps), None)
+    assert sm(x=None) == -1 and ln(y=None) == -1
+    assert sm(R=0) == -3 and ln(N=0) == -3
+    assert sm(R=1 << 20, N=1 << 20) == -3                 # R * N >= 2^40
+    assert sm(x=X + 8) == -4 and ln(g=G + 2) == -4
+    assert sm(scale=0.0) == -8 and sm(scale=-1.0) == -8 and sm(scale=float("nan")) == -8
+    assert ln(eps=0.0) == -8 and ln(eps=float("inf")) == -8
+    assert sm(y=X + 16) == -7                              # partial overlap
+    assert ln(g=Y + 64) == -7                              # gamma inside the output
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert sm(y=X) == -6                               # in place passes the host checks
+        assert ln(b=G + 4096) == -6
+    assert attnio.stream_rows_cached(65536) and attnio.stream_rows_cached(8)
+    assert not attnio.stream_rows_cached(65544) and not attnio.stream_rows_cached(1001)
 
 
 @pytest.mark.parametrize("name", ["attn_fwd", "attn_fwd_f32"])
