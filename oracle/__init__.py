@@ -15,6 +15,8 @@ from .attention import (  # noqa: F401
     attention_bwd_sampled_fp64,
     attention_rows_fp64,
     decode_bf16_bits,
+    decode_e4m3_bits,
+    attention_fp8_fp64,
     effective_kv_len,
     to_fp64,
 )

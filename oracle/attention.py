@@ -53,6 +53,8 @@ __all__ = [
     "attention_bwd_fp64",
     "attention_bwd_rows_fp64",
     "attention_bwd_sampled_fp64",
+    "decode_e4m3_bits",
+    "attention_fp8_fp64",
 ]
 
 
@@ -67,6 +69,22 @@ def decode_bf16_bits(bits: np.ndarray) -> np.ndarray:
     if b.dtype != np.uint16:
         raise TypeError(f"bf16 bits must be uint16, got {b.dtype}")
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def decode_e4m3_bits(bits: np.ndarray) -> np.ndarray:
+    """Widen raw 8-bit float patterns of the OCP E4M3 ("e4m3fn") format to
+    float64, exactly: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 holds the subnormals m/8 * 2^-6; the all-ones pattern
+    S.1111.111 is NaN and there are no infinities (largest finite 448)."""
+    b = np.asarray(bits)
+    if b.dtype != np.uint8:
+        raise TypeError(f"e4m3 bits must be uint8, got {b.dtype}")
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = ((b >> 3) & 0xF).astype(np.int64)
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    nan = (e == 15) & (m == 7)
+    return np.where(nan, np.nan, sign * mag)
 
 
 def to_fp64(x: np.ndarray, kind: str) -> np.ndarray:
@@ -341,3 +359,26 @@ def attention_bwd_sampled_fp64(q, k, v, do, scale: float, causal: bool, kv_len, 
             dV[ksel] += P[:, cols].T @ dOf[r]
             dK[ksel] += s64 * (dS[:, cols].T @ Qf[r])
     return dQ, dK, dV
+
+
+def attention_fp8_fp64(q8, k8, v8, descale, scale: float, causal: bool = False, kv_len=None,
+                       rows=None, magnitude: bool = False):
+    """Exact attention of fp8 (OCP E4M3) inputs in fp64.
+
+    q8, k8, v8: uint8 bit patterns [B, H, N, d]; descale = (q_s, k_s, v_s): the
+    fp32 factors that turn each tensor's fp8 values into the real inputs
+    (x = fp8(bits) * s).  The real inputs are formed exactly in fp64 and the
+    attention operator graph is applied to them as in attention_fp64.
+
+    magnitude: also return M = |P| |V| (the probabilities applied to the
+    absolute values), same shape as the output: the scale of the error that
+    rounding the probabilities to fp8 can cause in each output element."""
+    qs, ks, vs = (float(np.float32(x)) for x in descale)
+    Q = decode_e4m3_bits(np.asarray(q8)) * qs
+    K = decode_e4m3_bits(np.asarray(k8)) * ks
+    V = decode_e4m3_bits(np.asarray(v8)) * vs
+    out = attention_fp64(Q, K, V, scale, causal, kv_len, kind="f64", rows=rows)
+    if not magnitude:
+        return out
+    mag = attention_fp64(Q, K, np.abs(V), scale, causal, kv_len, kind="f64", rows=rows)
+    return out, mag

@@ -523,3 +523,39 @@ def test_sampled_backward_late_keys_causal():
     np.testing.assert_allclose(got[0], dense[0][0, 0, rows], rtol=0, atol=1e-12)
     np.testing.assert_allclose(got[1], dense[1][0, 0, keys], rtol=0, atol=1e-12)
     np.testing.assert_allclose(got[2], dense[2][0, 0, keys], rtol=0, atol=1e-12)
+
+
+def test_e4m3_decoder_known_patterns():
+    bits = np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x39, 0x7E, 0xB8, 0x80, 0x30, 0x44, 0xFE], dtype=np.uint8)
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 448.0, -1.0, -0.0, 0.5, 3.0, -448.0]
+    got = oracle.decode_e4m3_bits(bits)
+    np.testing.assert_array_equal(got, want)
+    assert np.isnan(oracle.decode_e4m3_bits(np.array([0x7F, 0xFF], dtype=np.uint8))).all()
+
+
+def test_e4m3_decoder_matches_torch_on_all_patterns():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    bits = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_e4m3_bits(bits)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def test_fp8_attention_is_attention_of_the_decoded_inputs():
+    """Brute force on the exactly decoded, rescaled inputs; the magnitude output
+    is the attention of |V|, which bounds |O| elementwise."""
+    rng = np.random.default_rng(77)
+    B, H, N, d = 1, 2, 9, 4
+    # every sign, subnormals included, magnitudes below 4 (exponent field <= 8)
+    finite = np.array([b for b in range(256) if ((b >> 3) & 0xF) <= 8], dtype=np.uint8)
+    q8, k8, v8 = (rng.choice(finite, size=(B, H, N, d)) for _ in range(3))
+    ds = (0.25, 0.5, 2.0)
+    out, mag = oracle.attention_fp8_fp64(q8, k8, v8, ds, 0.1, True, None, magnitude=True)
+    dec = oracle.decode_e4m3_bits
+    Q, K, V = dec(q8) * 0.25, dec(k8) * 0.5, dec(v8) * 2.0
+    want = brute_force(Q, K, V, 0.1, True, None)
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-12)
+    assert (np.abs(out) <= mag + 1e-12).all()
