@@ -16,6 +16,7 @@ a bounded row sample on the host cores (which also checks those rows).
   python bench.py --mode bwd [--workload NAME]   # the backward (bf16 workloads)
   python bench.py --mode unfused [--workload NAME] [--heads-per-pass G]
   python bench.py --mode rows [--workload softmax_r32k_n32k|layernorm_r128k_n8k]
+  python bench.py --mode fp8 [--workload NAME]   # the workload's shape with E4M3 inputs
   python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
 
 In --mode bwd one step is one attn_bwd call (its three kernels) from the
@@ -381,6 +382,76 @@ def bench_rows(args) -> int:
     return 0
 
 
+def bench_fp8(w, args) -> int:
+    """The fp8 (E4M3) forward on the workload's shape: same seeded draws,
+    quantized per tensor with power-of-two descales; bf16 output.  Same
+    algorithmic FLOPs as the bf16 forward; roofline = the fp8 matrix peak."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_long_sequence_amd import attnio
+    from exact_long_sequence_amd.inputs import make_fp8_inputs, sample_rows
+    FP8_PEAK = 5000.0
+    dev = torch.device("cuda:0")
+    q8, k8, v8, ds, kv_len = make_fp8_inputs(w.B, w.H, w.N, w.d, w.seed, w.padded, w.q_mul)
+    qd, kd, vd = q8.to(dev), k8.to(dev), v8.to(dev)
+    kvd = None if kv_len is None else kv_len.to(dev)
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    # FLOPs do not depend on the element size; the model takes 2- or 4-byte elements
+    model = attnio.attn_io_model(w.B, w.H, w.N, w.d, 2, w.causal,
+                                 None if kv_len is None else kv_len.tolist())
+    fn = lambda: attnio.attn_fwd_fp8(qd, kd, vd, ds, causal=w.causal, kv_len=kvd, scale=w.scale,  # noqa: E731
+                                     out=out)
+    for _ in range(args.warmup):
+        fn()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    tflops = model["flops"] / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "attention fwd TFLOP/s, fp8 E4M3 inputs (algorithmic 4*d per visible pair)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulation, bf16 output)",
+        "data": "synthetic (seeded N(0,1) Q/K/V quantized per tensor)",
+        "config": {**w.describe(), "dtype": "fp8-e4m3", "descale": list(ds)},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": FP8_PEAK, "unit": "TFLOP/s",
+                     "frac": tflops / FP8_PEAK, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        rows = sample_rows(w.B, w.H, w.N, 256, w.seed)
+        t0 = time.perf_counter()
+        want = oracle.attention_fp8_fp64(q8.numpy(), k8.numpy(), v8.numpy(), ds, w.scale, w.causal,
+                                         None if kv_len is None else kv_len.numpy(), rows=rows)
+        dt = time.perf_counter() - t0
+        L = oracle.effective_kv_len(None if kv_len is None else kv_len.numpy(), w.B, w.N)
+        i = rows % w.N
+        Lr = L[(rows // w.N) // w.H]
+        keys = np.minimum(i + 1, Lr) if w.causal else Lr
+        got = out.reshape(-1, w.d).index_select(0, torch.as_tensor(rows, device=dev)).float().cpu().numpy()
+        result["cpu_baseline"] = {
+            "value": 4.0 * w.d * float(keys.sum()) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{rows.size} seeded query rows (fp8 decode of the whole tensors included), {dt:.1f} s",
+            "parity_on_sample": {"max_abs_err": float(np.abs(got - want).max())}}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,7 +461,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
-    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused", "rows"), default="fwd")
+    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused", "rows", "fp8"), default="fwd")
     ap.add_argument("--heads-per-pass", type=int, default=8,
                     help="--mode unfused: heads whose N x N intermediates share the workspace")
     args = ap.parse_args()
@@ -417,6 +488,8 @@ def main() -> int:
         return bench_bwd(w, args)
     if args.mode == "unfused":
         return bench_unfused(w, args)
+    if args.mode == "fp8":
+        return bench_fp8(w, args)
     dev = torch.device("cuda:0")
     q, k, v, kv_len = workload_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)

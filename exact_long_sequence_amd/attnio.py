@@ -22,7 +22,7 @@ ATTN_OK = 0
 
 __all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
-           "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_strerror", "attn_version", "attn_query_tiling",
+           "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_fwd_fp8", "attn_strerror", "attn_version", "attn_query_tiling",
            "attn_io_model", "library_path", "load_library"]
 
 
@@ -62,6 +62,8 @@ def load_library() -> ctypes.CDLL:
     lib.stream_layernorm.restype = i32
     lib.stream_rows_cached.argtypes = [i32]
     lib.stream_rows_cached.restype = i32
+    lib.attn_fwd_fp8.argtypes = [vp] * 4 + [i32] * 4 + [f32] * 4 + [i32, vp, vp]
+    lib.attn_fwd_fp8.restype = i32
     lib.attn_strerror.argtypes = [i32]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -346,4 +348,40 @@ def stream_layernorm(x: torch.Tensor, gamma: Optional[torch.Tensor] = None,
         rc = lib.stream_layernorm(x.data_ptr(), ptrs[0], ptrs[1], out.data_ptr(), R, N, float(eps), stream)
     if rc != ATTN_OK:
         raise RuntimeError(f"stream_layernorm: {attn_strerror(rc)} (code {rc})")
+    return out
+
+
+def attn_fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale, *,
+                 causal: bool = False, kv_len: Optional[torch.Tensor] = None,
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp8 (OCP E4M3) attention forward: q8, k8, v8 are uint8 (or float8_e4m3fn)
+    [B, H, N, d] device tensors, descale = (q_s, k_s, v_s) with x = fp8 * s.
+    Returns bf16 [B, H, N, d]."""
+    lib = load_library()
+    ts = []
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a GPU tensor")
+        if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+            raise TypeError(f"{name} must hold E4M3 bytes (uint8 or float8_e4m3fn), got {t.dtype}")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+        ts.append(t)
+    if not (q8.shape == k8.shape == v8.shape) or not (q8.device == k8.device == v8.device):
+        raise ValueError("q8, k8, v8 must share one shape and device")
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    elif out.shape != q8.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q8.device:
+        raise ValueError("out must be a contiguous bf16 tensor of q8's shape")
+    qs, ks, vs = (float(x) for x in descale)
+    kv_len, kv_ptr = _kv_len_ptr(kv_len, B, q8.device)
+    with torch.cuda.device(q8.device):
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+        rc = lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), B, H, N, d,
+                              float(scale), qs, ks, vs, int(bool(causal)), kv_ptr, stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_fp8: {attn_strerror(rc)} (code {rc})")
     return out

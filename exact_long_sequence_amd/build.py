@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattnio.so")
-SOURCES = ["attnio_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip"]
+SOURCES = ["attnio_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip", "attn_fwd_fp8.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit; hipcc -O3
 # would otherwise form v_pk_{add,mul,fma}_f32 from plain float code.

@@ -1,0 +1,263 @@
+// Exact attention forward with fp8 (OCP E4M3) Q, K, V on gfx950's fp8 matrix
+// cores; bf16 output.
+//
+// Same streamed schedule as the bf16 kernel ("From Attention Graph to
+// FlashAttention - A Memory-Centric Compilation Approach in AICF", section 3:
+// load a Q tile, stream K/V tiles, partial scores, online softmax update,
+// accumulate), with the quantisation that the Neural Circuit Diagrams
+// abstract lists among the effects its performance model covers:
+//   * Q, K, V arrive as E4M3 bytes with one fp32 descale per tensor
+//     (x = fp8 * s); S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 with
+//     unit block scales, and the descales fold into the softmax constant;
+//   * the probabilities are rounded to E4M3 for O^T += V^T P^T on the same
+//     instruction.  The exponent shift is held at (running row maximum - 8),
+//     so every probability lies in (0, 256] (E4M3's largest finite value is
+//     448) and the row's largest entries sit at the top of the format, where
+//     its relative step is 2^-3; the shift moves, and the accumulator is
+//     rescaled, only when a tile raises the running maximum;
+//   * the row sum l accumulates the unrounded fp32 probabilities; O is
+//     O^T * v_s / l, rounded to bf16 once.
+//
+// Workgroup: 4 waves x 32 query rows, 128-key K and V tiles through a
+// two-stage LDS ring of direct-to-LDS loads.  Each lane owns one query (S^T
+// orientation: row statistics are lane-local, the two 16-key halves of a
+// 32-key block sit in lanes l and l + 32).  V^T operands come from
+// ds_read_b64_tr_b8 transposes whose key order matches the order in which the
+// probabilities are packed into the B operand.
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "tile_ops.h"
+
+namespace attnio {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFp8Shift = 8;  // log2 of the largest probability (256)
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // format 0 (E4M3) for both operands, block scales 127 (= 2^0)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16-byte chunk swizzle of an LDS row of RB bytes (as for bf16 rows).
+template <int RB>
+__device__ __forceinline__ int swz8(int row) {
+  constexpr int RPB = 256 / RB;
+  constexpr int CH = RB / 16;
+  return (row / RPB) % CH;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2)
+void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+                         const uint8_t* __restrict__ V, __bf16* __restrict__ O,
+                         const int32_t* __restrict__ kv_len, int H, int N, float c, float vs,
+                         int n_qtiles) {
+  constexpr int THREADS = 256, BN = 128, BM = 128, RB = D;  // RB: bytes per row
+  constexpr int KT = BN * RB;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, half = lane / 32, col = lane % 32;
+  const int bh = blockIdx.x / n_qtiles;
+  int qt = blockIdx.x % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest first
+  const int b = bh / H;
+  int L = N;
+  if (kv_len != nullptr) {
+    L = kv_len[b];
+    L = L < 0 ? 0 : (L > N ? N : L);
+  }
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int q0 = qt * BM;
+  int kend = L;
+  if (CAUSAL) kend = min(kend, min(N, q0 + BM));
+  const int ntiles = (kend + BN - 1) / BN;
+  const size_t slice = (size_t)bh * N * RB;
+  const int qrow = q0 + wave * 32 + col;
+
+  // Q of this lane's query as B operands: bytes 64 ks + 32 half .. + 31
+  i32x8 qf[D / 64];
+  {
+    const int qr = qrow < N ? qrow : N - 1;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks) {
+      const i32x4* p = (const i32x4*)(Q + slice + (size_t)qr * RB + ks * 64 + half * 32);
+      const i32x4 lo = p[0], hi = p[1];
+      qf[ks] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;  // running row maximum of s * c (base-2 domain)
+  float l_run = 0.f;        // this lane's share of the row sum
+
+  if (ntiles > 0) {
+    const __bf16* Ks = (const __bf16*)(K + slice);  // byte base; dma_rows counts bytes
+    const __bf16* Vs = (const __bf16*)(V + slice);
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      const uint32_t st = lds_base + (uint32_t)((t & 1) * 2 * KT);
+      dma_rows<D / 2, BN, THREADS>(Ks, t * BN, kend - 1, st, wave, lane);
+      dma_rows<D / 2, BN, THREADS>(Vs, t * BN, kend - 1, st + KT, wave, lane);
+    };
+    issue(0);
+    wait_dma();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) issue(t + 1);
+      const char LDS_AS* kt_l = smem + (t & 1) * 2 * KT;
+      const char LDS_AS* vt_l = kt_l + KT;
+      const int j0 = t * BN;
+
+      // S^T = K Q^T: lane (h, c) holds keys (r/4)*8 + 4h + r%4 of block kb, query c
+      f32x16 s[BN / 32];
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        const int row = kb * 32 + col;
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+          const int ch = ks * 4 + half * 2;
+          const char LDS_AS* rp = kt_l + row * RB;
+          const i32x4 lo = *(const i32x4 LDS_AS*)(rp + ((ch ^ swz8<RB>(row)) * 16));
+          const i32x4 hi = *(const i32x4 LDS_AS*)(rp + (((ch + 1) ^ swz8<RB>(row)) * 16));
+          const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          s[kb] = mfma_fp8(a, qf[ks], s[kb]);
+        }
+      }
+      // scale into the base-2 domain and mask
+      const bool need_mask = (j0 + BN > L) || (CAUSAL && j0 + BN - 1 > q0);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = s[kb][r] * c;
+          if (need_mask) {
+            const int key = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+            bool ok = key < L;
+            if (CAUSAL) ok = ok && key <= qrow;
+            v = ok ? v : -INFINITY;
+          }
+          s[kb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // the shift follows the running maximum: rescale only when it rises
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        if (m_new != m_run) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+      }
+      const float sh = m_run == -INFINITY ? 0.f : m_run - (float)kFp8Shift;
+      // P = 2^(s - sh) in (0, 256]; packed as E4M3 B operands: operand ps, byte
+      // t = 16 b + r holds block 2 ps + b, register r
+      i32x8 pb[BN / 64];
+      float lt = 0.f;
+#pragma unroll
+      for (int ps = 0; ps < BN / 64; ++ps)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int kb = 2 * ps + w / 4, r0 = 4 * (w % 4);
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(s[kb][r0 + e] - sh);
+            lt += p[e];
+          }
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+          pb[ps][w] = word;
+        }
+      l_run += lt;
+      // O^T += V^T P^T: V^T by transpose reads.  Read u of operand (ps, db):
+      // lane 16g + 2e + q supplies key (2ps + u/2)*32 + (2(u%2) + e/4)*8 + 4h + e%4
+      // (h = g/2), bytes 32 db + 16 (g%2) + 8 q .. + 7; lane 16g + i receives
+      // byte i of those 8 keys, i.e. bytes t = 8u + e of its operand.
+      {
+        const int g = lane / 16, h = g / 2, e = (lane % 16) / 2, q = lane % 2;
+#pragma unroll
+        for (int ps = 0; ps < BN / 64; ++ps)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            i32x8 a;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int key = (2 * ps + u / 2) * 32 + (2 * (u % 2) + e / 4) * 8 + 4 * h + e % 4;
+              const int ch = 2 * db + (g % 2);
+              const char LDS_AS* ap = vt_l + key * RB + ((ch ^ swz8<RB>(key)) * 16) + q * 8;
+              const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)ap);
+              a[2 * u] = v2[0];
+              a[2 * u + 1] = v2[1];
+            }
+            oacc[db] = mfma_fp8(a, pb[ps], oacc[db]);
+          }
+      }
+      wait_dma();
+      __syncthreads();
+    }
+  }
+
+  // row sum over the two lanes of the query; lane (h, c) holds d rows
+  // db*32 + (r/4)*8 + 4h + r%4 of O^T for its query
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? vs / l_tot : 0.f;
+  if (qrow < N) {
+    __bf16* orow = O + (size_t)bh * N * D + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(oacc[db][a4 * 4 + e] * inv);
+        *(bf16x4*)(orow + db * 32 + a4 * 8 + half * 4) = o;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
+  const int n_qtiles = (a.N + 127) / 128;
+  const long long grid = (long long)a.B * a.H * n_qtiles;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float c = a.scale * a.q_descale * a.k_descale * kLog2e;
+  constexpr int lds = 2 * 2 * 128 * D;
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, stream,
+                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o,
+                     a.kv_len, a.H, a.N, c, a.v_descale, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
+  if (a.d == 128) return a.causal ? launch_fp8_t<128, true>(a, stream) : launch_fp8_t<128, false>(a, stream);
+  if (a.d == 64) return a.causal ? launch_fp8_t<64, true>(a, stream) : launch_fp8_t<64, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attnio

@@ -200,6 +200,31 @@ int attn_fwd_unfused(const void* Q, const void* K, const void* V, void* O, void*
   return ATTN_OK;
 }
 
+int attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                 float scale, float q_descale, float k_descale, float v_descale, int causal,
+                 const int32_t* kv_len, void* stream) {
+  if (!Q || !K || !V || !O) return ATTN_E_NULL;
+  if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
+  if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return ATTN_E_ALIGN;
+  if (!std::isfinite(scale)) return ATTN_E_ARG;
+  for (float s : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(s) || !(s > 0.f)) return ATTN_E_ARG;
+  const size_t in_b = (size_t)B * H * N * d, out_b = 2 * in_b;
+  if (ranges_overlap(O, out_b, Q, in_b) || ranges_overlap(O, out_b, K, in_b) ||
+      ranges_overlap(O, out_b, V, in_b))
+    return ATTN_E_ALIAS;
+  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  attnio::Fp8Args a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0,
+                    q_descale, k_descale, v_descale};
+  const hipError_t e = attnio::launch_fwd_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (log_enabled()) fprintf(stderr, "[attnio] fp8 launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
 namespace {
 int run_rows(const void* X, const void* gamma, const void* beta, void* Y, int R, int N, int op,
              float param, void* stream) {

@@ -75,7 +75,21 @@ struct RowArgs {
   float param;
 };
 
+// fp8 (E4M3) forward: Q, K, V bytes with per-tensor descales, bf16 O.
+struct Fp8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* kv_len;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  float q_descale, k_descale, v_descale;
+};
+
 bool bf16_tiling(int d, int causal, Tiling* t);
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int rows_cached_sweeps(int N);
 hipError_t launch_stream_rows(const RowArgs& a, hipStream_t stream);
 size_t unfused_head_bytes(int N);

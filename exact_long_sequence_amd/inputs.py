@@ -22,7 +22,7 @@ import math
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "oracle_view", "sample_rows", "RowWorkload",
+__all__ = ["Workload", "WORKLOADS", "quantize_e4m3", "make_fp8_inputs", "make_inputs", "oracle_view", "sample_rows", "RowWorkload",
            "ROW_WORKLOADS", "row_workload_inputs"]
 
 
@@ -166,3 +166,24 @@ def row_workload_inputs(w: RowWorkload):
     gamma = (1.0 + 0.1 * torch.randn((w.N,), generator=g, dtype=torch.float32)).to(torch.bfloat16)
     beta = (0.1 * torch.randn((w.N,), generator=g, dtype=torch.float32)).to(torch.bfloat16)
     return x, gamma, beta
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Round an fp32 tensor to OCP E4M3 with one power-of-two descale chosen so
+    that the largest magnitude lands at or below 448: returns (uint8 bits,
+    descale) with x ~= fp8(bits) * descale.  A power of two keeps the descale
+    exact in every precision."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    s = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
+    q = (x / s).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), s
+
+
+def make_fp8_inputs(B: int, H: int, N: int, d: int, seed: int = 0, padded: bool = False,
+                    q_mul: float = 1.0, kv_lo: int | None = None):
+    """fp8 inputs: the fp32 draws of make_inputs (same generator order), each
+    tensor quantized by quantize_e4m3.  Returns (q8, k8, v8, (q_s, k_s, v_s),
+    kv_len) on the CPU."""
+    q, k, v, kv_len = make_inputs(B, H, N, d, "f32", seed, padded, q_mul, kv_lo)
+    (q8, qs), (k8, ks), (v8, vs) = (quantize_e4m3(t) for t in (q, k, v))
+    return q8, k8, v8, (qs, ks, vs), kv_len

@@ -116,6 +116,20 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
  * only; 0 for non-positive sizes). */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
+/* fp8 attention forward (quantisation effects, as the Neural Circuit Diagrams
+ * abstract lists them among what its performance model covers).  Q, K, V are
+ * OCP E4M3 ("e4m3fn") bytes, contiguous [B, H, N, d], all finite; the real
+ * inputs are x = fp8(x) * x_descale with one finite, positive fp32 descale per
+ * tensor.  O is bf16 [B, H, N, d] (2 bytes per element; must not overlap the
+ * inputs).  Q K^T and P V run on gfx950's fp8 matrix cores with fp32
+ * accumulation; the probabilities are rounded to E4M3 (in (0, 256] relative to
+ * the running row maximum) for the P V product, the row sum uses the unrounded
+ * fp32 probabilities, and O is rounded to bf16 once.  Other conventions
+ * (d, N, scale, causal, kv_len, stream, errors) as for attn_fwd. */
+int attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                 float scale, float q_descale, float k_descale, float v_descale, int causal,
+                 const int32_t* kv_len, void* stream);
+
 /* Operator-centric (unfused) bf16 forward, the baseline the fused kernel is
  * measured against ("From Attention Graph to FlashAttention - A Memory-Centric
  * Compilation Approach in AICF", section 2: one kernel per operator, each

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = set(declared_functions())
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
-            "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_strerror", "attn_version",
+            "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_fwd_fp8", "attn_strerror",
+            "attn_version",
             "attn_query_tiling", "attn_io_model"} <= names
 
 
@@ -128,6 +129,21 @@ def test_unfused_entry_argument_errors(lib):
     assert call(w=ws + 16) == -4                   # workspace must be 256-byte aligned
     assert call(nbytes=need - 1) == -8             # less than one head
     assert call(w=0x6000000 - 256) == -7           # workspace overlaps O
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert call() == -6
+
+
+def test_fp8_entry_argument_errors(lib):
+    def call(q=0x100000, o=0x400000, d=64, N=16, scale=0.125, qs=1.0, ks=1.0, vs=1.0):
+        return lib.attn_fwd_fp8(q, 0x200000, 0x300000, o, 1, 1, N, d, ctypes.c_float(scale),
+                                ctypes.c_float(qs), ctypes.c_float(ks), ctypes.c_float(vs), 0, None, None)
+    assert call(q=None) == -1 and call(o=None) == -1
+    assert call(d=96) == -2 and call(N=0) == -3
+    assert call(q=0x100008) == -4
+    assert call(scale=float("nan")) == -8
+    assert call(qs=0.0) == -8 and call(ks=-1.0) == -8 and call(vs=float("inf")) == -8
+    assert call(o=0x300000 - 1024) == -7       # 2 KiB of bf16 output reaches into V's 1 KiB
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         assert call() == -6
