@@ -1,28 +1,42 @@
 """Builds the HIP library libattnio.so in-tree for gfx950 with hipcc.
 
+Each translation unit is compiled to an object of its own (in parallel, into a
+temporary directory), then the objects are linked into one shared library.
+
 Usage:  python -m exact_long_sequence_amd.build
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattnio.so")
-SOURCES = ["attnio_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip", "attn_fwd_fp8.hip"]
+SOURCES = ["attnio_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
+           "attn_bwd_dq_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip", "attn_fwd_fp8.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit; hipcc -O3
 # would otherwise form v_pk_{add,mul,fma}_f32 from plain float code.
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+
+# Per-file options.  The dQ kernel consumes MFMA results on the VALU; asking
+# the compiler for the VGPR form of MFMA keeps those results out of the
+# accumulation registers and removes the register-to-register copies (measured
+# faster; the dK/dV kernel, at the register limit, measured slower with it).
+FILE_FLAGS = {
+    "attn_bwd_dq_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def hipcc() -> str:
@@ -32,18 +46,33 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 HIP library cannot be built")
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[:3])} ...")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    cc = hipcc()
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="attnio_build_") as tmpdir:
+        objs, cmds = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            objs.append(obj)
+            cmds.append([cc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *inc, "-c",
+                         os.path.join(CSRC, src), "-o", obj])
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB_PATH + ".tmp"
+        _run([cc, *HIPCC_FLAGS, "-shared", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
 

@@ -7,13 +7,15 @@
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = dO_i . O_i,
 //     dQ = s dS K,   dK = s dS^T Q.
 // Three kernels, enqueued in this order on the caller's stream:
-//   delta: D_i = dO_i . O_i and lse_i * log2(e) per row, into the workspace;
+//   delta: D_i = dO_i . O_i and lse_i * log2(e) per row, into the workspace
+//          (padding rows of each head get D = 0, lse = +inf);
 //   dk_dv: one workgroup per (batch*head, 128 keys); K and V of those keys stay
 //          in registers as MFMA operands while Q, dO and the row statistics of
-//          64-row query blocks stream through a two-stage LDS ring (DMA of the
-//          next block under the current one);
+//          64-row query blocks stream through a three-stage LDS ring; the S and
+//          dP MFMAs of block i+1 run under the P / dS arithmetic of block i;
 //   dq:    one workgroup per (batch*head, 128 queries); Q and dO stay in
-//          registers while 64-key K/V tiles stream through the LDS ring.
+//          registers while 64-key K/V tiles stream through an LDS ring (its own
+//          translation unit, attn_bwd_dq_bf16.hip, built with other options).
 // Both recompute S and dP; each keeps its accumulators (dK^T, dV^T or dQ^T) in
 // registers for its whole loop and writes them once, so no atomics and no
 // partial sums reach memory.  Every product is a bf16 MFMA 32x32x16 with fp32
@@ -41,6 +43,7 @@ namespace attnio {
 namespace {
 
 constexpr int kStatPad = 64;  // workspace rows are padded per head to a multiple of this
+constexpr int kBwdBQ = 64;  // query rows per dK/dV pipeline step (32 measured slower)
 
 // ----------------------------------------------------------------------------
 // delta: D_i = dO_i . O_i (fp32) and lse_i * log2(e), per row.
@@ -49,13 +52,20 @@ template <int D>
 __global__ __launch_bounds__(256)
 void attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
                            const float* __restrict__ lse, float* __restrict__ ws_d,
-                           float* __restrict__ ws_l, int N, int NP, long long rows) {
+                           float* __restrict__ ws_l, int N, int NP, long long rows_p) {
+  // one row of the padded [B*H][NP] statistics per LPR lanes; padding rows
+  // (i >= N) get D = 0 and lse = +inf, so a block that reads them computes
+  // P = 2^(s c - inf) = 0 and dS = 0 without a select
   constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gid / LPR;
+  const long long rp = gid / LPR;
   const int part = (int)(gid % LPR);
+  const long long bh = rp / NP;
+  const int i = (int)(rp % NP);
+  const bool real = rp < rows_p && i < N;
+  const long long row = bh * N + i;
   float acc = 0.f;
-  if (row < rows) {
+  if (real) {
     const bf16x8 o = *(const bf16x8*)(O + row * D + part * 8);
     const bf16x8 g = *(const bf16x8*)(dO + row * D + part * 8);
 #pragma unroll
@@ -63,17 +73,32 @@ void attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restric
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off, LPR);
-  if (row < rows && part == 0) {
-    const long long bh = row / N, i = row % N;
-    ws_d[bh * NP + i] = acc;
-    ws_l[bh * NP + i] = lse[row] * kLog2e;
+  if (rp < rows_p && part == 0) {
+    ws_d[rp] = real ? acc : 0.f;
+    ws_l[rp] = real ? lse[row] * kLog2e : INFINITY;
   }
 }
 
 // ----------------------------------------------------------------------------
-// dk_dv: 4 waves x 32 keys; 64-row query blocks through a two-stage LDS ring.
+// dk_dv: 4 waves x 32 keys; 64-row query blocks through a three-stage LDS ring.
+//
+// One wave per SIMD, software-pipelined across query blocks: while the MFMAs of
+// S and dP for block i+1 run, the same wave computes P and dS of block i on the
+// VALU (one score per MFMA slot, the slots pinned by scheduling barriers);
+// then the dV / dK MFMAs of block i.  The loop body is instantiated twice with
+// the two S / dP register sets swapping roles, so nothing is copied.
 // ----------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int BQ_>
+struct KvCfg {
+  static constexpr int WAVES = 4, THREADS = 256, BQ = BQ_, BKV = 32 * WAVES;
+  static constexpr int RB = 2 * D;
+  static constexpr int QT = BQ * RB;            // one Q or dO block
+  static constexpr int STAGE = 2 * QT + 1024;   // Q, dO, row statistics (one 64-lane load)
+  static constexpr int STAGES = 3;
+  static constexpr int LDS = STAGES * STAGE;
+};
+
+template <int D, bool CAUSAL, int BQ_>
 __global__ __launch_bounds__(256, 1)
 void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -81,10 +106,9 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                           __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                           const int32_t* __restrict__ kv_len, int H, int N, int NP, float c,
                           float scale, int n_kblocks) {
-  constexpr int WAVES = 4, THREADS = 256, BQ = 64, BKV = 32 * WAVES;
-  constexpr int RB = 2 * D;
-  constexpr int QT = BQ * RB;             // one Q or dO tile
-  constexpr int STAGE = 2 * QT + 1024;    // Q, dO, row statistics
+  using C = KvCfg<D, BQ_>;
+  constexpr int NB = BQ_ / 32;  // 32-row halves per query block
+  constexpr int BQ = C::BQ, BKV = C::BKV, QT = C::QT, STAGE = C::STAGE;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
@@ -92,7 +116,20 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, col = lane % 32;
-  const int bh = blockIdx.x / n_kblocks, kblk = blockIdx.x % n_kblocks;
+  // XCD-aware assignment: block x runs on XCD x % 8; when B*H is a multiple of
+  // 8, head j's key blocks all run on XCD j % 8 (its Q and dO stream through
+  // one L2), key block 0 (the longest causal loop) first
+  int bh, kblk;
+  {
+    const int G = gridDim.x, x = blockIdx.x, xcd = x % 8, idx = x / 8;
+    if ((G / n_kblocks) % 8 == 0) {
+      bh = xcd + 8 * (idx / n_kblocks);
+      kblk = idx % n_kblocks;
+    } else {
+      bh = x / n_kblocks;
+      kblk = x % n_kblocks;
+    }
+  }
   const int b = bh / H;
   int L = N;
   if (kv_len != nullptr) {
@@ -128,81 +165,161 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const int nqb = (N + BQ - 1) / BQ - qb0;
     const __bf16* Qs = Q + slice;
     const __bf16* dOs = dO + slice;
+    const bool key_ok = key < L;
+    auto stage_of = [&](int i) __attribute__((always_inline)) { return (i % C::STAGES) * STAGE; };
     auto issue = [&](int i) __attribute__((always_inline)) {
       const int q0 = (qb0 + i) * BQ;
-      const uint32_t st = lds_base + (uint32_t)((i & 1) * STAGE);
-      dma_rows<D, BQ, THREADS>(Qs, q0, N - 1, st, wave, lane);
-      dma_rows<D, BQ, THREADS>(dOs, q0, N - 1, st + QT, wave, lane);
+      const uint32_t st = lds_base + (uint32_t)stage_of(i);
+      dma_rows<D, BQ, C::THREADS>(Qs, q0, N - 1, st, wave, lane);
+      dma_rows<D, BQ, C::THREADS>(dOs, q0, N - 1, st + QT, wave, lane);
       if (wave == 0) {
-        // lanes 0-15: lse*log2e of the 64 rows, 16-31: D, 32-63 repeat 0-31
-        // (the two workspace arrays are l_off floats apart)
-        const int sub = lane % 32;
-        const uint32_t off = (uint32_t)(((sub < 16 ? l_off : 0LL) + (long long)bh * NP + q0 + 4 * (sub % 16)) * 4);
+        // lanes 0 .. BQ/4-1: lse*log2e of the BQ rows, the next BQ/4: D, the
+        // rest repeat them (the two workspace arrays are l_off floats apart)
+        constexpr int NL = BQ / 4;
+        const int sub = lane % (2 * NL);
+        const uint32_t off = (uint32_t)(((sub < NL ? l_off : 0LL) + (long long)bh * NP + q0 + 4 * (sub % NL)) * 4);
         dma16(ws_d, off, __builtin_amdgcn_readfirstlane(st + 2 * QT));
       }
     };
-    issue(0);
-    wait_dma();
-    __syncthreads();
-    for (int i = 0; i < nqb; ++i) {
-      if (i + 1 < nqb) issue(i + 1);
-      const char LDS_AS* qt_l = smem + (i & 1) * STAGE;
-      const char LDS_AS* dot_l = qt_l + QT;
-      const float LDS_AS* st_l = (const float LDS_AS*)(qt_l + 2 * QT);
-      const int q0 = (qb0 + i) * BQ;
 
-      // S = Q K^T and dP = dO V^T for two 32-row blocks; lane (h, c) holds
-      // rows (r/4)*8 + 4h + r%4 of each block, column = its key
-      f32x16 s[2], dp[2];
+    // MFMA slot m of S / dP for one block: accumulator m % (2 NB) (S or dP of
+    // one of the block's 32-row halves), k step m / (2 NB)
+    auto qk_read = [&](const char LDS_AS* st_l, int m) __attribute__((always_inline)) {
+      const int acc = m % (2 * NB), ks = m / (2 * NB);
+      const char LDS_AS* tile = st_l + ((acc % 2) ? QT : 0);
+      return row_operand<D>(tile, (acc / 2) * 32 + col, ks, half);
+    };
+    auto qk_mfma = [&](f32x16 (&s)[NB], f32x16 (&dp)[NB], const bf16x8& a, int m)
+        __attribute__((always_inline)) {
+      const int acc = m % (2 * NB), ks = m / (2 * NB), blk = acc / 2;
+      const f32x16 zero = {};
+      if (acc % 2 == 0)
+        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], ks == 0 ? zero : s[blk], 0, 0, 0);
+      else
+        dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], ks == 0 ? zero : dp[blk], 0, 0, 0);
+    };
+    constexpr int NQK = 2 * NB * (D / 16);  // MFMAs of S and dP per block
+    constexpr int NEL = 16 * NB;            // scores per lane per block
+    constexpr int R = 4;               // LDS read-ahead (MFMA slots)
+
+    // S / dP of block i alone (prologue)
+    auto qk_only = [&](int i, f32x16 (&s)[NB], f32x16 (&dp)[NB]) __attribute__((always_inline)) {
+      const char LDS_AS* st_l = smem + stage_of(i);
+      bf16x8 ring[R + 1];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int m = 0; m < R; ++m) ring[m] = qk_read(st_l, m);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { s[blk][r] = 0.f; dp[blk][r] = 0.f; }
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 aq = row_operand<D>(qt_l, blk * 32 + col, ks, half);
-          s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[blk], 0, 0, 0);
-          const bf16x8 ad = row_operand<D>(dot_l, blk * 32 + col, ks, half);
-          dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[ks], dp[blk], 0, 0, 0);
-        }
+      for (int m = 0; m < NQK; ++m) {
+        if (m + R < NQK) ring[(m + R) % (R + 1)] = qk_read(st_l, m + R);
+        qk_mfma(s, dp, ring[m % (R + 1)], m);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // P = 2^(S c - lse2), dS = P (dP - D); packed as B operands of the
-      // query-contracting products: operand st covers rows 16 st .. 16 st + 15
+    };
+
+    // P and dS of one score (element m of NEL) of block i, into the packed B
+    // operands: operand st covers block rows 16 st .. 16 st + 15.  MASKED
+    // blocks apply the key-padding / causal / last-row masks per score.
+    auto pds_elem = [&](auto masked_c, const f32x16 (&s)[NB], const f32x16 (&dp)[NB],
+                        const float LDS_AS* st_f, int q0, int m, f32x4& l4, f32x4& d4,
+                        bf16x8 (&pp)[BQ / 16], bf16x8 (&pds)[BQ / 16]) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_c)::value;
+      const int blk = m / 16, a4 = (m % 16) / 4, e = m % 4, r = a4 * 4 + e;
+      const int ql = blk * 32 + a4 * 8 + half * 4;  // first of four consecutive rows
+      if (e == 0) {
+        l4 = *(const f32x4 LDS_AS*)(st_f + ql);
+        d4 = *(const f32x4 LDS_AS*)(st_f + BQ + ql);
+      }
+      float arg = __builtin_fmaf(s[blk][r], c, -l4[e]);
+      if (MASKED) {
+        // bitwise, not short-circuit: no exec-mask branches per score; the
+        // exponent is selected, not the result, so no branch forms around exp2
+        const int q = q0 + ql + e;
+        bool ok = key_ok & (q < N);
+        if (CAUSAL) ok = ok & (key <= q);
+        arg = ok ? arg : -INFINITY;
+      }
+      const float p = __builtin_amdgcn_exp2f(arg);
+      const float ds = p * (dp[blk][r] - d4[e]);  // p = 0 exactly where masked
+      const int st = blk * 2 + a4 / 2, t8 = (a4 % 2) * 4 + e;
+      pp[st][t8] = (__bf16)p;
+      pds[st][t8] = (__bf16)ds;
+    };
+
+    // dV^T += dO^T P, dK^T += Q^T dS for block i: slot m -> (st, db, dv|dk)
+    auto pv_stream = [&](int i, const bf16x8 (&pp)[BQ / 16], const bf16x8 (&pds)[BQ / 16])
+        __attribute__((always_inline)) {
+      const char LDS_AS* qt_l = smem + stage_of(i);
+      const char LDS_AS* dot_l = qt_l + QT;
+      constexpr int NPV = (BQ / 16) * (D / 32) * 2;
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        const int which = m % 2, db = (m / 2) % (D / 32), st = m / 2 / (D / 32);
+        return tr_operand<D>(which ? qt_l : dot_l, db, st, lane);
+      };
+      bf16x8 ring[R + 1];
+#pragma unroll
+      for (int m = 0; m < R; ++m) ring[m] = rd(m);
+#pragma unroll
+      for (int m = 0; m < NPV; ++m) {
+        if (m + R < NPV) ring[(m + R) % (R + 1)] = rd(m + R);
+        const int which = m % 2, db = (m / 2) % (D / 32), st = m / 2 / (D / 32);
+        if (which == 0)
+          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[m % (R + 1)], pp[st], dvt[db], 0, 0, 0);
+        else
+          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[m % (R + 1)], pds[st], dkt[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // one step: S / dP of block i+1 (if any) computed under P / dS of block i,
+    // then dV / dK of block i
+    auto step_m = [&](auto masked_c, int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB],
+                      f32x16 (&dpn)[NB]) __attribute__((always_inline)) {
+      if (i + 2 < nqb) issue(i + 2);
+      const char LDS_AS* cur = smem + stage_of(i);
+      const float LDS_AS* st_f = (const float LDS_AS*)(cur + 2 * QT);
+      const int q0 = (qb0 + i) * BQ;
       bf16x8 pp[BQ / 16], pds[BQ / 16];
-      const bool key_ok = key < L;
+      f32x4 l4, d4;
+      if (i + 1 < nqb) {
+        const char LDS_AS* nxt = smem + stage_of(i + 1);
+        bf16x8 ring[R + 1];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+        for (int m = 0; m < R; ++m) ring[m] = qk_read(nxt, m);
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int ql = blk * 32 + a4 * 8 + half * 4;  // first of four consecutive rows
-          const f32x4 l4 = *(const f32x4 LDS_AS*)(st_l + ql);
-          const f32x4 d4 = *(const f32x4 LDS_AS*)(st_l + 64 + ql);
+        for (int m = 0; m < NQK; ++m) {
+          if (m + R < NQK) ring[(m + R) % (R + 1)] = qk_read(nxt, m + R);
+          qk_mfma(sn, dpn, ring[m % (R + 1)], m);
+          // NEL scores over the NQK slots
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = a4 * 4 + e;
-            const int q = q0 + ql + e;
-            bool ok = key_ok && q < N;
-            if (CAUSAL) ok = ok && key <= q;
-            const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][r], c, -l4[e])) : 0.f;
-            const float ds = ok ? p * (dp[blk][r] - d4[e]) : 0.f;
-            const int st = blk * 2 + a4 / 2, t8 = (a4 % 2) * 4 + e;
-            pp[st][t8] = (__bf16)p;
-            pds[st][t8] = (__bf16)ds;
-          }
+          for (int e = m * NEL / NQK; e < (m + 1) * NEL / NQK; ++e)
+            pds_elem(masked_c, s, dp, st_f, q0, e, l4, d4, pp, pds);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      // dV^T += dO^T P,  dK^T += Q^T dS
+      } else {
 #pragma unroll
-      for (int st = 0; st < BQ / 16; ++st)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a1 = tr_operand<D>(dot_l, db, st, lane);
-          dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, pp[st], dvt[db], 0, 0, 0);
-          const bf16x8 a2 = tr_operand<D>(qt_l, db, st, lane);
-          dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, pds[st], dkt[db], 0, 0, 0);
-        }
-      wait_dma();
+        for (int e = 0; e < NEL; ++e) pds_elem(masked_c, s, dp, st_f, q0, e, l4, d4, pp, pds);
+      }
+      pv_stream(i, pp, pds);
+      if (i + 2 < nqb) wait_dma_n<0>();
       __syncthreads();
+    };
+    // (every block takes the masked path: a second, unmasked instance of the
+    // step doubles the live registers and spills)
+    auto step = [&](int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB], f32x16 (&dpn)[NB])
+        __attribute__((always_inline)) { step_m(std::true_type{}, i, s, dp, sn, dpn); };
+
+    issue(0);
+    if (nqb > 1) issue(1);
+    wait_dma_n<0>();
+    __syncthreads();
+    f32x16 sA[NB], dpA[NB], sB[NB], dpB[NB];
+    qk_only(0, sA, dpA);
+    int i = 0;
+    for (; i + 1 < nqb; i += 2) {
+      step(i, sA, dpA, sB, dpB);
+      step(i + 1, sB, dpB, sA, dpA);
     }
+    if (i < nqb) step(i, sA, dpA, sB, dpB);
   }
 
   // lane (h, c) holds rows db*32 + (r/4)*8 + 4h + r%4 (head dimension) of its key
@@ -225,145 +342,13 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   }
 }
 
-// ----------------------------------------------------------------------------
-// dq: 4 waves x 32 queries; 64-key K/V tiles through a two-stage LDS ring.
-// ----------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1)
-void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                        const float* __restrict__ ws_d, const float* __restrict__ ws_l,
-                        __bf16* __restrict__ dQ, const int32_t* __restrict__ kv_len, int H, int N,
-                        int NP, float c, float scale, int n_qtiles) {
-  constexpr int WAVES = 4, THREADS = 256, BN = 64, BM = 32 * WAVES;
-  constexpr int RB = 2 * D;
-  constexpr int KT = BN * RB;       // one K or V tile
-  constexpr int STAGE = 2 * KT;
-  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
-  char LDS_AS* smem = (char LDS_AS*)smem_raw;
-  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int lane = tid % 64, half = lane / 32, col = lane % 32;
-  const int bh = blockIdx.x / n_qtiles;
-  int qt = blockIdx.x % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest first
-  const int b = bh / H;
-  int L = N;
-  if (kv_len != nullptr) {
-    L = kv_len[b];
-    L = L < 0 ? 0 : (L > N ? N : L);
-  }
-  L = __builtin_amdgcn_readfirstlane(L);
-  const int q0 = qt * BM;
-  int kend = L;
-  if (CAUSAL) kend = min(kend, min(N, q0 + BM));
-  const int ntiles = (kend + BN - 1) / BN;
-  const size_t slice = (size_t)bh * N * D;
-  const int qrow = q0 + wave * 32 + col;  // the query this lane owns
-
-  bf16x8 qf[D / 16], dof[D / 16];
-  float lse2 = 0.f, dlt = 0.f;
-  {
-    const int qr = qrow < N ? qrow : N - 1;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = *(const bf16x8*)(Q + slice + (size_t)qr * D + ks * 16 + half * 8);
-      dof[ks] = *(const bf16x8*)(dO + slice + (size_t)qr * D + ks * 16 + half * 8);
-    }
-    lse2 = ws_l[(size_t)bh * NP + qr];
-    dlt = ws_d[(size_t)bh * NP + qr];
-  }
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(dof[ks]));
-  asm volatile("" ::"v"(lse2), "v"(dlt));
-
-  f32x16 dqt[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
-
-  if (ntiles > 0) {
-    const __bf16* Ks = K + slice;
-    const __bf16* Vs = V + slice;
-    auto issue = [&](int t) __attribute__((always_inline)) {
-      const uint32_t st = lds_base + (uint32_t)((t & 1) * STAGE);
-      dma_rows<D, BN, THREADS>(Ks, t * BN, kend - 1, st, wave, lane);
-      dma_rows<D, BN, THREADS>(Vs, t * BN, kend - 1, st + KT, wave, lane);
-    };
-    issue(0);
-    wait_dma();
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      if (t + 1 < ntiles) issue(t + 1);
-      const char LDS_AS* kt_l = smem + (t & 1) * STAGE;
-      const char LDS_AS* vt_l = kt_l + KT;
-      const int j0 = t * BN;
-      // S^T = K Q^T and dP^T = V dO^T: lane (h, c) holds keys (r/4)*8 + 4h + r%4
-      // of each 32-key block for its query c
-      f32x16 s[BN / 32], dp[BN / 32];
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 ak = row_operand<D>(kt_l, kb * 32 + col, ks, half);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s[kb], 0, 0, 0);
-          const bf16x8 av = row_operand<D>(vt_l, kb * 32 + col, ks, half);
-          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], dp[kb], 0, 0, 0);
-        }
-      }
-      // dS^T = P^T (dP^T - D), packed as B operands of dQ^T += K^T dS^T
-      bf16x8 pds[BN / 16];
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
-#pragma unroll
-          for (int t8 = 0; t8 < 8; ++t8) {
-            const int r = sp * 8 + t8;
-            const int kk = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            bool ok = kk < L;
-            if (CAUSAL) ok = ok && kk <= qrow;
-            const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2)) : 0.f;
-            pds[kb * 2 + sp][t8] = (__bf16)(ok ? p * (dp[kb][r] - dlt) : 0.f);
-          }
-#pragma unroll
-      for (int st = 0; st < BN / 16; ++st)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a = tr_operand<D>(kt_l, db, st, lane);
-          dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pds[st], dqt[db], 0, 0, 0);
-        }
-      wait_dma();
-      __syncthreads();
-    }
-  }
-
-  if (qrow < N) {
-    __bf16* orow = dQ + slice + (size_t)qrow * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        bf16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(dqt[db][a4 * 4 + e] * scale);
-        *(bf16x4*)(orow + db * 32 + a4 * 8 + half * 4) = o;
-      }
-  }
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int NP = (a.N + kStatPad - 1) / kStatPad * kStatPad;
   float* ws_d = a.ws;
   float* ws_l = a.ws + (size_t)a.B * a.H * NP;
-  const long long rows = (long long)a.B * a.H * a.N;
-  const long long dgrid = (rows * (D / 8) + 255) / 256;
+  const long long rows_p = (long long)a.B * a.H * NP;
+  const long long dgrid = (rows_p * (D / 8) + 255) / 256;
   const int n_kblocks = (a.N + 127) / 128;
   const int n_qtiles = (a.N + 127) / 128;
   const long long g_kv = (long long)a.B * a.H * n_kblocks;
@@ -371,22 +356,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (dgrid > 0x7fffffffLL || g_kv > 0x7fffffffLL || g_q > 0x7fffffffLL) return hipErrorInvalidValue;
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)dgrid), dim3(256), 0, stream,
-                     (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, ws_d, ws_l, a.N, NP, rows);
+                     (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, ws_d, ws_l, a.N, NP, rows_p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int kv_lds = 2 * (2 * 64 * 2 * D + 1024);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g_kv), dim3(256), kv_lds,
+  constexpr int kv_lds = KvCfg<D, kBwdBQ>::LDS;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, kBwdBQ>), dim3((unsigned)g_kv), dim3(256), kv_lds,
                      stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                      (const __bf16*)a.dout, ws_d, (long long)(ws_l - ws_d), (__bf16*)a.dk,
                      (__bf16*)a.dv, a.kv_len, a.H, a.N, NP, c, a.scale, n_kblocks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int q_lds = 2 * 2 * 64 * 2 * D;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g_q), dim3(256), q_lds, stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                     (const __bf16*)a.dout, ws_d, ws_l, (__bf16*)a.dq, a.kv_len, a.H, a.N, NP, c,
-                     a.scale, n_qtiles);
-  return hipGetLastError();
+  return launch_bwd_dq_bf16(a, ws_d, ws_l, NP, c, stream);
 }
 
 }  // namespace

@@ -1,0 +1,178 @@
+// dQ kernel of the bf16 attention backward (gfx950).  Launched by
+// launch_bwd_bf16 after the delta kernel has written the row statistics.
+//
+// One workgroup per (batch*head, 128 queries), 4 waves x 32 queries, in the
+// forward's orientation: S^T = K Q^T and dP^T = V dO^T with the wave's 32
+// queries across the lanes (lse and D are lane-local); 64-key K/V tiles stream
+// through a two-stage LDS ring; dQ^T += K^T dS^T with K^T by transpose reads;
+// dQ is scaled and written once.  Causal tiles stop at their diagonal and run
+// longest first.  This unit is compiled with the VGPR form of MFMA (the
+// products' results feed the VALU directly).
+
+#include <hip/hip_runtime.h>
+#include <float.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "tile_ops.h"
+
+namespace attnio {
+namespace {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1)
+void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                        const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                        const float* __restrict__ ws_d, const float* __restrict__ ws_l,
+                        __bf16* __restrict__ dQ, const int32_t* __restrict__ kv_len, int H, int N,
+                        int NP, float c, float scale, int n_qtiles) {
+  constexpr int WAVES = 4, THREADS = 256, BN = 64, BM = 32 * WAVES;
+  constexpr int RB = 2 * D;
+  constexpr int KT = BN * RB;       // one K or V tile
+  constexpr int STAGE = 2 * KT;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, half = lane / 32, col = lane % 32;
+  const int bh = blockIdx.x / n_qtiles;
+  int qt = blockIdx.x % n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest first
+  const int b = bh / H;
+  int L = N;
+  if (kv_len != nullptr) {
+    L = kv_len[b];
+    L = L < 0 ? 0 : (L > N ? N : L);
+  }
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int q0 = qt * BM;
+  int kend = L;
+  if (CAUSAL) kend = min(kend, min(N, q0 + BM));
+  const int ntiles = (kend + BN - 1) / BN;
+  const size_t slice = (size_t)bh * N * D;
+  const int qrow = q0 + wave * 32 + col;  // the query this lane owns
+
+  bf16x8 qf[D / 16], dof[D / 16];
+  float lse2 = 0.f, dlt = 0.f;
+  {
+    const int qr = qrow < N ? qrow : N - 1;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = *(const bf16x8*)(Q + slice + (size_t)qr * D + ks * 16 + half * 8);
+      dof[ks] = *(const bf16x8*)(dO + slice + (size_t)qr * D + ks * 16 + half * 8);
+    }
+    lse2 = ws_l[(size_t)bh * NP + qr];
+    dlt = ws_d[(size_t)bh * NP + qr];
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(dof[ks]));
+  asm volatile("" ::"v"(lse2), "v"(dlt));
+
+  f32x16 dqt[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
+
+  if (ntiles > 0) {
+    const __bf16* Ks = K + slice;
+    const __bf16* Vs = V + slice;
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      const uint32_t st = lds_base + (uint32_t)((t & 1) * STAGE);
+      dma_rows<D, BN, THREADS>(Ks, t * BN, kend - 1, st, wave, lane);
+      dma_rows<D, BN, THREADS>(Vs, t * BN, kend - 1, st + KT, wave, lane);
+    };
+    issue(0);
+    wait_dma();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) issue(t + 1);
+      const char LDS_AS* kt_l = smem + (t & 1) * STAGE;
+      const char LDS_AS* vt_l = kt_l + KT;
+      const int j0 = t * BN;
+      // S^T = K Q^T and dP^T = V dO^T: lane (h, c) holds keys (r/4)*8 + 4h + r%4
+      // of each 32-key block for its query c
+      f32x16 s[BN / 32], dp[BN / 32];
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 ak = row_operand<D>(kt_l, kb * 32 + col, ks, half);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s[kb], 0, 0, 0);
+          const bf16x8 av = row_operand<D>(vt_l, kb * 32 + col, ks, half);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], dp[kb], 0, 0, 0);
+        }
+      }
+      // dS^T = P^T (dP^T - D), packed as B operands of dQ^T += K^T dS^T
+      bf16x8 pds[BN / 16];
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+          for (int t8 = 0; t8 < 8; ++t8) {
+            const int r = sp * 8 + t8;
+            const int kk = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+            bool ok = kk < L;
+            if (CAUSAL) ok = ok && kk <= qrow;
+            const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2)) : 0.f;
+            pds[kb * 2 + sp][t8] = (__bf16)(ok ? p * (dp[kb][r] - dlt) : 0.f);
+          }
+#pragma unroll
+      for (int st = 0; st < BN / 16; ++st)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 a = tr_operand<D>(kt_l, db, st, lane);
+          dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pds[st], dqt[db], 0, 0, 0);
+        }
+      wait_dma();
+      __syncthreads();
+    }
+  }
+
+  if (qrow < N) {
+    __bf16* orow = dQ + slice + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(dqt[db][a4 * 4 + e] * scale);
+        *(bf16x4*)(orow + db * 32 + a4 * 8 + half * 4) = o;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const BwdArgs& a, const float* ws_d, const float* ws_l, int NP, float c,
+                       hipStream_t stream) {
+  const int n_qtiles = (a.N + 127) / 128;
+  const long long g_q = (long long)a.B * a.H * n_qtiles;
+  if (g_q > 0x7fffffffLL) return hipErrorInvalidValue;
+  constexpr int q_lds = 2 * 2 * 64 * 2 * D;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g_q), dim3(256), q_lds, stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                     (const __bf16*)a.dout, ws_d, ws_l, (__bf16*)a.dq, a.kv_len, a.H, a.N, NP, c,
+                     a.scale, n_qtiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* ws_d, const float* ws_l, int NP,
+                              float c, hipStream_t stream) {
+  if (a.d == 128)
+    return a.causal ? launch_dq_t<128, true>(a, ws_d, ws_l, NP, c, stream)
+                    : launch_dq_t<128, false>(a, ws_d, ws_l, NP, c, stream);
+  if (a.d == 64)
+    return a.causal ? launch_dq_t<64, true>(a, ws_d, ws_l, NP, c, stream)
+                    : launch_dq_t<64, false>(a, ws_d, ws_l, NP, c, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attnio

@@ -96,6 +96,10 @@ size_t unfused_head_bytes(int N);
 hipError_t launch_unfused_bf16(const UnfusedArgs& a, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+// dQ stage of the backward (ws_d / ws_l: the delta kernel's padded statistics,
+// NP rows per head; c = scale * log2(e)).
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* ws_d, const float* ws_l, int NP,
+                              float c, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 

@@ -34,6 +34,11 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
                :: "s"(lds), "v"(voff), "s"(gbase) : "memory");
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_dma_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // A operand of a 32x32x16 MFMA from an LDS tile of rows of D bf16: lane (h, c)
 // gets row `row`, columns 16 ks + 8 h .. + 7 (one 16-byte read).
