@@ -47,12 +47,42 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// 16-byte chunk swizzle of an LDS row of RB bytes (as for bf16 rows).
+// 16-byte chunk swizzle of an LDS row of RB bytes.  Both read patterns must
+// spread over distinct banks: 16 consecutive rows at one logical chunk (the K
+// operand reads) and, for the V transpose reads of lanes 0-31, rows
+// {c..c+3, c+8..c+11} (c a multiple of 4) at two adjacent logical chunks.
+// With 128-byte rows two rows share a 256-byte bank line; the line index
+// x = row/2 mod 8 maps to x with bits 0 and 1 swapped, which keeps the
+// line-pairs {x, x+1, x+4, x+5} of the second pattern in four different chunk
+// pairs.  64-byte rows (four per line) need only the line index mod 4.
 template <int RB>
 __device__ __forceinline__ int swz8(int row) {
-  constexpr int RPB = 256 / RB;
-  constexpr int CH = RB / 16;
-  return (row / RPB) % CH;
+  if (RB == 128) {
+    const int x = (row / 2) % 8;
+    return (x & 4) | ((x & 1) << 1) | ((x >> 1) & 1);
+  }
+  return (row / 4) % 4;
+}
+
+// Direct-to-LDS load of ROWS rows of RB bytes starting at global row r0 (rows
+// past last_ok clamped to it), laid out with swz8.
+template <int RB, int ROWS, int THREADS>
+__device__ __forceinline__ void dma_rows8(const uint8_t* gsrc, int r0, int last_ok, uint32_t lds_tile,
+                                          int wave, int lane) {
+  constexpr int LOADS = ROWS * RB / 16 / THREADS;
+  static_assert(ROWS * RB % (16 * THREADS) == 0, "tile must split evenly");
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = (i * THREADS + wave * 64 + lane) * 16;
+    const int row = pos / RB;
+    const int pch = (pos % RB) / 16;
+    const int lch = pch ^ swz8<RB>(row);
+    int grow = r0 + row;
+    grow = grow < last_ok ? grow : last_ok;
+    const uint32_t o = (uint32_t)(grow * RB + lch * 16);
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((i * THREADS + wave * 64) * 16));
+    dma16(gsrc, o, l);
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -70,9 +100,21 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, col = lane % 32;
-  const int bh = blockIdx.x / n_qtiles;
-  int qt = blockIdx.x % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest first
+  // XCD-aware assignment (block x runs on XCD x % 8): when B*H is a multiple
+  // of 8, head j's query tiles all run on XCD j % 8, so its K and V stream
+  // through one L2; causal tiles longest first
+  int bh, qt;
+  {
+    const int G = gridDim.x, x = blockIdx.x, xcd = x % 8, idx = x / 8;
+    if ((G / n_qtiles) % 8 == 0) {
+      bh = xcd + 8 * (idx / n_qtiles);
+      qt = idx % n_qtiles;
+    } else {
+      bh = x / n_qtiles;
+      qt = x % n_qtiles;
+    }
+  }
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
   const int b = bh / H;
   int L = N;
   if (kv_len != nullptr) {
@@ -108,12 +150,12 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
   float l_run = 0.f;        // this lane's share of the row sum
 
   if (ntiles > 0) {
-    const __bf16* Ks = (const __bf16*)(K + slice);  // byte base; dma_rows counts bytes
-    const __bf16* Vs = (const __bf16*)(V + slice);
+    const uint8_t* Ks = K + slice;
+    const uint8_t* Vs = V + slice;
     auto issue = [&](int t) __attribute__((always_inline)) {
       const uint32_t st = lds_base + (uint32_t)((t & 1) * 2 * KT);
-      dma_rows<D / 2, BN, THREADS>(Ks, t * BN, kend - 1, st, wave, lane);
-      dma_rows<D / 2, BN, THREADS>(Vs, t * BN, kend - 1, st + KT, wave, lane);
+      dma_rows8<RB, BN, THREADS>(Ks, t * BN, kend - 1, st, wave, lane);
+      dma_rows8<RB, BN, THREADS>(Vs, t * BN, kend - 1, st + KT, wave, lane);
     };
     issue(0);
     wait_dma();
@@ -141,23 +183,29 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
           s[kb] = mfma_fp8(a, qf[ks], s[kb]);
         }
       }
-      // scale into the base-2 domain and mask
+      // scale into the base-2 domain; mask (one uniform test per tile, not per
+      // score) only the tiles on the diagonal or past kv_len
       const bool need_mask = (j0 + BN > L) || (CAUSAL && j0 + BN - 1 > q0);
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] *= c;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+            bool ok = key < L;
+            if (CAUSAL) ok = ok & (key <= qrow);  // bitwise: no branch per score
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[kb][r] * c;
-          if (need_mask) {
-            const int key = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            bool ok = key < L;
-            if (CAUSAL) ok = ok && key <= qrow;
-            v = ok ? v : -INFINITY;
-          }
-          s[kb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       // the shift follows the running maximum: rescale only when it rises
       if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
