@@ -19,14 +19,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte chunk swizzle of an LDS row of D bf16 values (rows read 16 bytes per
-// lane by 32 consecutive rows stay on distinct banks).  Writes and every read of
-// a tile use the same function, so any XOR pattern is correct.
+// 16-byte chunk swizzle of an LDS row of D bf16 values.  A tile is read two
+// ways and both must spread over distinct banks:
+//   row reads        16 consecutive rows (aligned), one logical chunk each;
+//   transpose reads  4 consecutive rows (aligned to 4), 4 adjacent chunks each
+//                    (lanes 0-31 of ds_read_b64_tr_b16).
+// With x the row's bank-line index (row / rows-per-line, mod chunks-per-row),
+// the XOR pattern is a bijection of x (row reads) whose top two bits differ for
+// the 4 rows of a transpose read: x with its low bits rotated to the top
+// (d = 128: one row per line, x = row mod 16, the two 2-bit halves swapped;
+// d = 64: two rows per line, x = (row / 2) mod 8, bit 0 moved to bit 2).
+// Writes and every read of a tile use this function, so the layout is
+// consistent by construction.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  constexpr int RPB = 256 / (2 * D);   // rows per 256-byte bank line
-  constexpr int CH = 2 * D / 16;       // chunks per row
-  return (row / RPB) % CH;
+  if (D == 128) {
+    const int x = row % 16;
+    return ((x & 3) << 2) | (x >> 2);
+  }
+  const int x = (row / 2) % 8;
+  return ((x & 1) << 2) | (x >> 1);
 }
 
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
