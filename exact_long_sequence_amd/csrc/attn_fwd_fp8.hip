@@ -183,13 +183,16 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
           s[kb] = mfma_fp8(a, qf[ks], s[kb]);
         }
       }
-      // scale into the base-2 domain; mask (one uniform test per tile, not per
-      // score) only the tiles on the diagonal or past kv_len
+      // mask (one uniform test per tile, not per score) only the tiles on the
+      // diagonal or past kv_len.  Scores stay unscaled: a masked score becomes
+      // the infinity that maps to -inf under the scale c (never 0: the launcher
+      // replaces c = 0 by the smallest normal float, which leaves every
+      // visible probability exactly 1 relative to the shift), and the tile's
+      // largest scaled score is c times the raw maximum (c > 0) or minimum
+      // (c < 0), so the scaling costs one fma per score, inside exp2.
       const bool need_mask = (j0 + BN > L) || (CAUSAL && j0 + BN - 1 > q0);
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] *= c;
+      const bool pos = c > 0.f;
+      const float lose = pos ? -INFINITY : INFINITY;
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
@@ -198,15 +201,24 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
             const int key = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
             bool ok = key < L;
             if (CAUSAL) ok = ok & (key <= qrow);  // bitwise: no branch per score
-            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            s[kb][r] = ok ? s[kb][r] : lose;
           }
       }
-      float tmax = -INFINITY;
+      float ext = lose;
+      if (pos) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+          for (int r = 0; r < 16; ++r) ext = fmaxf(ext, s[kb][r]);
+        ext = fmaxf(ext, __shfl_xor(ext, 32));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ext = fminf(ext, s[kb][r]);
+        ext = fminf(ext, __shfl_xor(ext, 32));
+      }
+      const float tmax = ext * c;  // -inf when every score of the row is masked
       // the shift follows the running maximum: rescale only when it rises
       if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
         const float m_new = fmaxf(m_run, tmax);
@@ -233,7 +245,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
           float p[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(s[kb][r0 + e] - sh);
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + e], c, -sh));
             lt += p[e];
           }
           int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
@@ -292,7 +304,8 @@ hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
   const int n_qtiles = (a.N + 127) / 128;
   const long long grid = (long long)a.B * a.H * n_qtiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const float c = a.scale * a.q_descale * a.k_descale * kLog2e;
+  float c = a.scale * a.q_descale * a.k_descale * kLog2e;
+  if (c == 0.f) c = FLT_MIN;  // keeps masked scores at -inf (inf * 0 would be NaN)
   constexpr int lds = 2 * 2 * 128 * D;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o,

@@ -113,3 +113,16 @@ def test_fp8_headline_workload_sampled():
                                           rows=rows, magnitude=True)
     got = o.reshape(-1, d).index_select(0, torch.as_tensor(rows, device=DEV)).float().cpu().numpy()
     _check(got, want, mag, "headline")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.07])
+def test_fp8_zero_and_negative_scale(scale):
+    # scale 0 gives uniform weights over the visible keys; a negative scale
+    # favours the smallest scores; masking must hold in both
+    q8, k8, v8, ds, kv = make_fp8_inputs(2, 2, 300, 64, 4200, padded=True, kv_lo=0)
+    o = attnio.attn_fwd_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), ds, causal=True, kv_len=kv.to(DEV),
+                            scale=scale)
+    torch.cuda.synchronize()
+    want, mag = oracle.attention_fp8_fp64(_bits(q8), _bits(k8), _bits(v8), ds, scale, True, kv.numpy(),
+                                          magnitude=True)
+    _check(o.float().cpu().numpy(), want, mag, f"scale={scale}")
