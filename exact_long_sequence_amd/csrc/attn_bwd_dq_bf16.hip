@@ -6,7 +6,7 @@
 // queries across the lanes (lse and D are lane-local); 64-key K/V tiles stream
 // through a two-stage LDS ring; dQ^T += K^T dS^T with K^T by transpose reads;
 // dQ is scaled and written once.  Causal tiles stop at their diagonal and run
-// longest first.  This unit is compiled with the VGPR form of MFMA (the
+// longest first; a head's tiles share one XCD.  This unit is compiled with the VGPR form of MFMA (the
 // products' results feed the VALU directly).
 
 #include <hip/hip_runtime.h>
@@ -37,9 +37,21 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, col = lane % 32;
-  const int bh = blockIdx.x / n_qtiles;
-  int qt = blockIdx.x % n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest first
+  // XCD-aware assignment (block x runs on XCD x % 8): when B*H is a multiple
+  // of 8, head j's query tiles all run on XCD j % 8, so its K and V stream
+  // through one L2; causal tiles longest first
+  int bh, qt;
+  {
+    const int G = gridDim.x, x = blockIdx.x, xcd = x % 8, idx = x / 8;
+    if ((G / n_qtiles) % 8 == 0) {
+      bh = xcd + 8 * (idx / n_qtiles);
+      qt = idx % n_qtiles;
+    } else {
+      bh = x / n_qtiles;
+      qt = x % n_qtiles;
+    }
+  }
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
   const int b = bh / H;
   int L = N;
   if (kv_len != nullptr) {
