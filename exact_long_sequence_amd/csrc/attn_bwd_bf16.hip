@@ -34,8 +34,6 @@
 #include <float.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "kernels.h"
 #include "tile_ops.h"
 
@@ -165,7 +163,6 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const int nqb = (N + BQ - 1) / BQ - qb0;
     const __bf16* Qs = Q + slice;
     const __bf16* dOs = dO + slice;
-    const bool key_ok = key < L;
     auto stage_of = [&](int i) __attribute__((always_inline)) { return (i % C::STAGES) * STAGE; };
     auto issue = [&](int i) __attribute__((always_inline)) {
       const int q0 = (qb0 + i) * BQ;
@@ -217,12 +214,18 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     };
 
     // P and dS of one score (element m of NEL) of block i, into the packed B
-    // operands: operand st covers block rows 16 st .. 16 st + 15.  MASKED
-    // blocks apply the key-padding / causal / last-row masks per score.
-    auto pds_elem = [&](auto masked_c, const f32x16 (&s)[NB], const f32x16 (&dp)[NB],
-                        const float LDS_AS* st_f, int q0, int m, f32x4& l4, f32x4& d4,
-                        bf16x8 (&pp)[BQ / 16], bf16x8 (&pds)[BQ / 16]) __attribute__((always_inline)) {
-      constexpr bool MASKED = decltype(masked_c)::value;
+    // operands: operand st covers block rows 16 st .. 16 st + 15.
+    //
+    // Only the causal mask is applied per score.  Query rows at or past N need
+    // none: their workspace statistics (lse = +inf, D = 0) give P = 0 and
+    // dS = 0.  Keys at or past kv_len need none either: a key's P and dS only
+    // reach its own column of dV^T and dK^T, which the store replaces by zero.
+    // The causal test key <= q0 + 32 blk + 8 a4 + 4 half + e is one compare of
+    // the lane's tq = key - q0 - 4 half against a compile-time constant; the
+    // exponent is selected, not the result, so no branch forms around exp2.
+    auto pds_elem = [&](const f32x16 (&s)[NB], const f32x16 (&dp)[NB], const float LDS_AS* st_f,
+                        int tq, int m, f32x4& l4, f32x4& d4, bf16x8 (&pp)[BQ / 16],
+                        bf16x8 (&pds)[BQ / 16]) __attribute__((always_inline)) {
       const int blk = m / 16, a4 = (m % 16) / 4, e = m % 4, r = a4 * 4 + e;
       const int ql = blk * 32 + a4 * 8 + half * 4;  // first of four consecutive rows
       if (e == 0) {
@@ -230,14 +233,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         d4 = *(const f32x4 LDS_AS*)(st_f + BQ + ql);
       }
       float arg = __builtin_fmaf(s[blk][r], c, -l4[e]);
-      if (MASKED) {
-        // bitwise, not short-circuit: no exec-mask branches per score; the
-        // exponent is selected, not the result, so no branch forms around exp2
-        const int q = q0 + ql + e;
-        bool ok = key_ok & (q < N);
-        if (CAUSAL) ok = ok & (key <= q);
-        arg = ok ? arg : -INFINITY;
-      }
+      if (CAUSAL) arg = (tq <= blk * 32 + a4 * 8 + e) ? arg : -INFINITY;
       const float p = __builtin_amdgcn_exp2f(arg);
       const float ds = p * (dp[blk][r] - d4[e]);  // p = 0 exactly where masked
       const int st = blk * 2 + a4 / 2, t8 = (a4 % 2) * 4 + e;
@@ -272,12 +268,12 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
     // one step: S / dP of block i+1 (if any) computed under P / dS of block i,
     // then dV / dK of block i
-    auto step_m = [&](auto masked_c, int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB],
-                      f32x16 (&dpn)[NB]) __attribute__((always_inline)) {
+    auto step = [&](int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB], f32x16 (&dpn)[NB])
+        __attribute__((always_inline)) {
       if (i + 2 < nqb) issue(i + 2);
       const char LDS_AS* cur = smem + stage_of(i);
       const float LDS_AS* st_f = (const float LDS_AS*)(cur + 2 * QT);
-      const int q0 = (qb0 + i) * BQ;
+      const int tq = key - (qb0 + i) * BQ - half * 4;  // below 0 on every block past the diagonal
       bf16x8 pp[BQ / 16], pds[BQ / 16];
       f32x4 l4, d4;
       if (i + 1 < nqb) {
@@ -292,22 +288,17 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
           // NEL scores over the NQK slots
 #pragma unroll
           for (int e = m * NEL / NQK; e < (m + 1) * NEL / NQK; ++e)
-            pds_elem(masked_c, s, dp, st_f, q0, e, l4, d4, pp, pds);
+            pds_elem(s, dp, st_f, tq, e, l4, d4, pp, pds);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < NEL; ++e) pds_elem(masked_c, s, dp, st_f, q0, e, l4, d4, pp, pds);
+        for (int e = 0; e < NEL; ++e) pds_elem(s, dp, st_f, tq, e, l4, d4, pp, pds);
       }
       pv_stream(i, pp, pds);
       if (i + 2 < nqb) wait_dma_n<0>();
       __syncthreads();
     };
-    // (every block takes the masked path: a second, unmasked instance of the
-    // step doubles the live registers and spills)
-    auto step = [&](int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB], f32x16 (&dpn)[NB])
-        __attribute__((always_inline)) { step_m(std::true_type{}, i, s, dp, sn, dpn); };
-
     issue(0);
     if (nqb > 1) issue(1);
     wait_dma_n<0>();
@@ -322,8 +313,11 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     if (i < nqb) step(i, sA, dpA, sB, dpB);
   }
 
-  // lane (h, c) holds rows db*32 + (r/4)*8 + 4h + r%4 (head dimension) of its key
+  // lane (h, c) holds rows db*32 + (r/4)*8 + 4h + r%4 (head dimension) of its
+  // key; a key at or past kv_len gets zero gradients (its accumulators, built
+  // without a key mask, are discarded, not multiplied)
   if (key < N) {
+    const bool key_ok = key < L;
     __bf16* krow = dK + slice + (size_t)key * D;
     __bf16* vrow = dV + slice + (size_t)key * D;
 #pragma unroll
@@ -333,8 +327,8 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         bf16x4 ok4, ov4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ok4[e] = (__bf16)(dkt[db][a4 * 4 + e] * scale);
-          ov4[e] = (__bf16)(dvt[db][a4 * 4 + e]);
+          ok4[e] = (__bf16)(key_ok ? dkt[db][a4 * 4 + e] * scale : 0.f);
+          ov4[e] = (__bf16)(key_ok ? dvt[db][a4 * 4 + e] : 0.f);
         }
         *(bf16x4*)(krow + db * 32 + a4 * 8 + half * 4) = ok4;
         *(bf16x4*)(vrow + db * 32 + a4 * 8 + half * 4) = ov4;

@@ -65,6 +65,7 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const int ntiles = (kend + BN - 1) / BN;
   const size_t slice = (size_t)bh * N * D;
   const int qrow = q0 + wave * 32 + col;  // the query this lane owns
+  const int last = CAUSAL ? min(L - 1, qrow) : L - 1;  // its last visible key
 
   bf16x8 qf[D / 16], dof[D / 16];
   float lse2 = 0.f, dlt = 0.f;
@@ -119,7 +120,12 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dof[ks], dp[kb], 0, 0, 0);
         }
       }
-      // dS^T = P^T (dP^T - D), packed as B operands of dQ^T += K^T dS^T
+      // dS^T = P^T (dP^T - D), packed as B operands of dQ^T += K^T dS^T.  Key
+      // kk = j0 + 32 kb + 8 (r/4) + 4 half + r%4 is visible iff kk <= last
+      // (kk < kv_len and, causal, kk <= the query): one compare of a
+      // compile-time constant with the lane's tk per score, selecting the
+      // exponent (exp2(-inf) = 0, so dS = 0 too) rather than branching
+      const int tk = last - j0 - half * 4;
       bf16x8 pds[BN / 16];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
@@ -128,11 +134,10 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
           for (int t8 = 0; t8 < 8; ++t8) {
             const int r = sp * 8 + t8;
-            const int kk = j0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            bool ok = kk < L;
-            if (CAUSAL) ok = ok && kk <= qrow;
-            const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2)) : 0.f;
-            pds[kb * 2 + sp][t8] = (__bf16)(ok ? p * (dp[kb][r] - dlt) : 0.f);
+            const float arg = (kb * 32 + (r / 4) * 8 + (r % 4) <= tk)
+                                  ? __builtin_fmaf(s[kb][r], c, -lse2) : -INFINITY;
+            const float p = __builtin_amdgcn_exp2f(arg);
+            pds[kb * 2 + sp][t8] = (__bf16)(p * (dp[kb][r] - dlt));
           }
 #pragma unroll
       for (int st = 0; st < BN / 16; ++st)
