@@ -15,8 +15,10 @@
 //     448) and the row's largest entries sit at the top of the format, where
 //     its relative step is 2^-3; the shift moves, and the accumulator is
 //     rescaled, only when a tile raises the running maximum;
-//   * the row sum l accumulates the unrounded fp32 probabilities; O is
-//     O^T * v_s / l, rounded to bf16 once.
+//   * the row sum l is the sum of the same E4M3 probabilities that multiply
+//     V, formed on the matrix core (an all-ones operand times P), so O =
+//     O^T * v_s / l is an exact convex combination of V's rows up to the
+//     fp32 accumulation; O is rounded to bf16 once.
 //
 // Workgroup: 4 waves x 32 query rows, 128-key K and V tiles through a
 // two-stage LDS ring of direct-to-LDS loads.  Each lane owns one query (S^T
@@ -147,7 +149,15 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = -INFINITY;  // running row maximum of s * c (base-2 domain)
-  float l_run = 0.f;        // this lane's share of the row sum
+  // Row sum on the matrix core: an all-ones A operand (E4M3 1.0 = 0x38 in
+  // every byte) times the packed P gives, in every element of the lane's
+  // accumulator, the sum of the E4M3 probabilities of its query over the
+  // operand's 64 keys -- the same rounded values that multiply V.
+  const i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                       0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  f32x16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
 
   if (ntiles > 0) {
     const uint8_t* Ks = K + slice;
@@ -228,7 +238,8 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-          l_run *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
           m_run = m_new;
         }
       }
@@ -236,7 +247,6 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
       // P = 2^(s - sh) in (0, 256]; packed as E4M3 B operands: operand ps, byte
       // t = 16 b + r holds block 2 ps + b, register r
       i32x8 pb[BN / 64];
-      float lt = 0.f;
 #pragma unroll
       for (int ps = 0; ps < BN / 64; ++ps)
 #pragma unroll
@@ -244,15 +254,11 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
           const int kb = 2 * ps + w / 4, r0 = 4 * (w % 4);
           float p[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + e], c, -sh));
-            lt += p[e];
-          }
+          for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + e], c, -sh));
           int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
           pb[ps][w] = word;
         }
-      l_run += lt;
       // O^T += V^T P^T: V^T by transpose reads.  Read u of operand (ps, db):
       // lane 16g + 2e + q supplies key (2ps + u/2)*32 + (2(u%2) + e/4)*8 + 4h + e%4
       // (h = g/2), bytes 32 db + 16 (g%2) + 8 q .. + 7; lane 16g + i receives
@@ -275,15 +281,17 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
             }
             oacc[db] = mfma_fp8(a, pb[ps], oacc[db]);
           }
+#pragma unroll
+        for (int ps = 0; ps < BN / 64; ++ps) lacc = mfma_fp8(ones8, pb[ps], lacc);
       }
       wait_dma();
       __syncthreads();
     }
   }
 
-  // row sum over the two lanes of the query; lane (h, c) holds d rows
-  // db*32 + (r/4)*8 + 4h + r%4 of O^T for its query
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // lane (h, c) holds d rows db*32 + (r/4)*8 + 4h + r%4 of O^T for its
+  // query, and (in every element of lacc) the query's whole row sum
+  const float l_tot = lacc[0];
   const float inv = l_tot > 0.f ? vs / l_tot : 0.f;
   if (qrow < N) {
     __bf16* orow = O + (size_t)bh * N * D + (size_t)qrow * D;

@@ -4,16 +4,20 @@ fp64 oracle of the same fp8 inputs, through the C ABI.
 The oracle decodes the E4M3 bytes exactly and applies the descales, so input
 quantisation is not part of the error; what remains is the kernel's own
 rounding.  Tolerance, elementwise, derived from it:
-    |O - O_ref| <= 2^-4 M + 2^-9 |O_ref| + 2e-3,    M = |P| |V| (oracle),
+    |O - O_ref| <= (M + |O_ref|) / 15 + 2^-9 |O_ref| + 2e-3,   M = |P| |V| (oracle),
     mean |O - O_ref| <= 2^-6 mean(M).
-Each probability is rounded to E4M3 once; in the format's normal range the
-relative error is at most 2^-4, so the output moves by at most 2^-4 sum_j P_j
-|V_j| = 2^-4 M; the output's bf16 rounding adds 2^-9 |O|.  Probabilities in
-E4M3's subnormal range (below 2^-14 of the row maximum, since the kernel keeps
-the maximum at 256) round with an absolute error of at most 2^-18 of the
-maximum each; with the fp32 accumulation they stay far inside the 2e-3 term
-(a CPU model of exactly these roundings exceeds the first two terms by at most
-2e-6 on the shapes below, and its mean error is at most 0.46% of mean(M)).
+Each probability is rounded to E4M3 once, p_j (1 + d_j) with |d_j| <= 2^-4 in
+the format's normal range, and the row sum is the sum of those same rounded
+values, so O = sum_j P_j (1 + d_j) V_j / (1 + db) with db = sum_j P_j d_j:
+O - O_ref = (sum_j P_j d_j V_j - db O_ref) / (1 + db), at most
+2^-4 (M + |O_ref|) / (1 - 2^-4) = (M + |O_ref|) / 15; the output's bf16
+rounding adds 2^-9 |O|.  Probabilities in E4M3's subnormal range (below 2^-14
+of the row maximum, since the kernel keeps the maximum at 256) round with an
+absolute error of at most 2^-18 of the maximum each; with the fp32
+accumulation they stay far inside the 2e-3 term (a CPU model of exactly these
+roundings, per-tile shifts included, exceeds the first two terms by at most
+5e-6 on the shapes below, reaches at most 0.59 of the bound, and its mean
+error is at most 0.63% of mean(M)).
 """
 
 import math
@@ -40,7 +44,7 @@ def _check(got, want, mag, label):
     got = np.asarray(got, dtype=np.float64)
     assert np.isfinite(got).all(), f"{label}: non-finite output"
     err = np.abs(got - want)
-    bound = 2.0 ** -4 * mag + 2.0 ** -9 * np.abs(want) + 2e-3
+    bound = (mag + np.abs(want)) / 15.0 + 2.0 ** -9 * np.abs(want) + 2e-3
     bad = err > bound
     ratio = float(np.max(err / bound)) if err.size else 0.0
     mean_ok = err.mean() <= 2.0 ** -6 * mag.mean() + 1e-12 if err.size else True
