@@ -19,22 +19,30 @@
 // wave's 32 queries across the 32 lanes) makes every softmax statistic
 // lane-local: each lane owns one query, its 16 values per 32x32 block are that
 // query's scores for 16 keys, and the other 16 keys of the block sit in the
-// lane 32 apart.  The row max therefore needs one permlane32 swap per tile, the
-// row sum none until the epilogue, and the rescale of the output accumulator
-// is one multiply by a per-lane scalar.  The accumulator O^T has the same
+// lane 32 apart.  The row max therefore needs one permlane32 swap per tile,
+// and the rescale of the output accumulator is one multiply by a per-lane
+// scalar.  The row sum is either lane-local too (two-element dot products,
+// merged across the lane pair in the epilogue) or, at d = 128, formed on the
+// matrix core (a 0/1 selection operand times P, next to the P x V MFMAs),
+// which leaves two VALU operations per score (fma, exp) and one conversion
+// per pair.  The accumulator O^T has the same
 // lane = query layout, and the probabilities come out of the score MFMA
 // already in the B-operand layout of the P x V MFMA.  This is the "parallel
 // execution pattern for efficient softmax" of "I/O Analysis is All You Need:
 // An I/O Analysis for Long-Sequence Attention" (abstract, optimisation 3)
 // mapped onto 64-wide wavefronts.
 //
-// The shift of the exponentials is lazy.  Any shift at or below the row
-// maximum gives the same softmax (it cancels between numerator and
-// denominator), so the shift is taken from the first key tile's row maxima
-// and moved again only when a tile's row sum shows that some probability
-// would exceed 2^16 (then to the current maxima, rescaling the running output
-// and row sum).  The result is exact up to rounding, every probability stays
-// in [0, 2^16], and the per-tile row maximum is not needed on the common path.
+// The shift of the exponentials is lazy.  Any shift gives the same softmax
+// (it cancels between numerator and denominator), so the shift is taken from
+// the first key tile's row maxima and moved again only when a tile's row sum
+// shows a probability above 2^16 (by that sum's power of two, rescaling the
+// running output and row sum).  The per-tile row maximum is not needed on the
+// common path.  A VALU row sum is tested before the tile's P x V (the tile is
+// recomputed after moving the shift).  A matrix-core row sum is known one
+// MFMA phase after its P, so the test comes after the tile's P x V; if an
+// exp2 overflowed there (a score more than 2^7 above the shift in the base-2
+// domain), the workgroup computes its rows again with the shift checked
+// before every tile.
 //
 // Two loop forms share the per-tile building blocks (selected per head size
 // at the bottom of this file):
@@ -64,6 +72,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
@@ -72,6 +81,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTauLog2 = 8.0f;        // shift moves when a row maximum exceeds it by 2^8
 constexpr float kLazySumMax = 65536.f;  // a tile row sum above this recomputes the shift
+
+// Where the row sums of P are formed: on the matrix core (next to the P x V
+// MFMAs, one tile late) or on the VALU (two-element dot products, in the
+// softmax).  Measured on MI355X: the same speed at d = 128 (the kernel runs at
+// a power-limited clock, and the two cost about the same energy), while at
+// d = 64 the VALU form lets two workgroups share a CU without register spills.
+#ifndef ATTNIO_RS_MFMA_D128
+#define ATTNIO_RS_MFMA_D128 1
+#endif
+#ifndef ATTNIO_RS_MFMA_D64
+#define ATTNIO_RS_MFMA_D64 0
+#endif
+constexpr bool rowsum_on_mfma(int d) {
+  return d == 128 ? ATTNIO_RS_MFMA_D128 != 0 : ATTNIO_RS_MFMA_D64 != 0;
+}
 
 template <int D, int BN, int WAVES, int NSTAGES>
 struct Cfg {
@@ -148,9 +172,23 @@ constexpr int kReadAhead = 4;
 
 // One MFMA phase as a single stream of MFMAs:
 //   DO_PV: O^T (D x 32 queries) += V_tile^T P^T   ((BN/16) x (D/32) MFMAs)
+//          and, when formed there, the tile's row sums of P
+//                                                  (BN/16 MFMAs, 16x16x32)
 //   DO_QK: S^T (BN keys x 32 queries) = K_tile Q^T ((D/16) x (BN/32) MFMAs)
 // in that order.  Each group of D/32 (resp. BN/32) consecutive MFMAs writes
-// independent accumulators, so dependent MFMAs are at least 4 apart.
+// independent accumulators, so dependent MFMAs are at least 3 apart.
+//
+// Row sums on the matrix core.  The 16x16x32 instruction reads a B operand of
+// 32 k x 16 columns with lane 16g + j holding k = 8g .. 8g + 7 of column j, so
+// the P operand of one 16-key step (lane 32h + c: keys 8h .. 8h + 7 of query
+// c) is, to it, column j = c % 16 with lane groups g = 2h + c / 16.  The
+// selection operand `sel` has rows 0 and 8 equal to 1 on the groups of even g
+// (query j) and rows 4 and 12 equal to 1 on the groups of odd g (query
+// j + 16), all else 0.  Output row 4g' of column j lands in lane 16g' + j, so
+// element 0 of every lane's 4-float result is the sum of its own query's 16
+// probabilities of the step, over both halves of the wave.  These are the same
+// bf16-rounded values that multiply V, so l matches the numerator exactly in
+// what it sums.
 //
 // The V operand uses the transpose read: lane 16g + 4j + q supplies V row
 // (16 st + 8u + 4h + j), columns 32 db + 16 (g % 2) + 4 q .. +3, and lane
@@ -162,9 +200,9 @@ constexpr int kReadAhead = 4;
 // read-ahead distance.
 template <class C, int D, int BN, bool DO_PV, bool DO_QK>
 __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 (&pb)[BN / 16],
-                                            f32x16 (&acc)[D / 32], const char LDS_AS* kl,
-                                            const bf16x8 (&qf)[D / 16], f32x16 (&s)[BN / 32],
-                                            int lane) {
+                                            f32x16 (&acc)[D / 32], const bf16x8& sel, f32x4& lsum,
+                                            const char LDS_AS* kl, const bf16x8 (&qf)[D / 16],
+                                            f32x16 (&s)[BN / 32], int lane) {
   const int half = lane / 32, col = lane % 32;
   const int g = lane / 16;
   const int jr = (lane % 16) / 4;
@@ -173,17 +211,34 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
   constexpr int NQK = DO_QK ? (D / 16) * (BN / 32) : 0;
   constexpr int NM = NPV + NQK;
   constexpr int R = kReadAhead;
+  // Every operand address is the lane's base address of this tile XOR a
+  // compile-time constant, plus an immediate row offset.  The swizzles are
+  // XORs on the chunk index with a period that divides the row steps, and the
+  // tile bases are multiples of the tile size, so
+  //   K: row kb*32 + col, chunk (2 ks + half) ^ swz_k(col)
+  //      = (kbase ^ 32 ks) + kb * 32 rows,
+  //   V: row st*16 + u*8 + 4 half + jr, chunk (2 db + ...) ^ swz_v(4 half + jr)
+  //      = (vbase ^ 64 db) + (st*16 + u*8) rows.
+  // Only the two bases are live across the phase: the empty asm hides their
+  // value, so the compiler forms each offset where it is used instead of
+  // keeping one register per distinct offset for the whole key loop.
+  static_assert(32 % (C::ROWS_PER_256 * C::CHUNKS) == 0 && 8 % (4 * C::ROWS_PER_256) == 0,
+                "swizzle periods must divide the operand row steps");
+  uint32_t kbase =
+      (uint32_t)(uintptr_t)kl + (uint32_t)(col * C::ROW_BYTES + ((half ^ swz_k<C>(col)) * 16));
+  const int vrow = half * 4 + jr;
+  uint32_t vbase = (uint32_t)(uintptr_t)vl +
+                         (uint32_t)(vrow * C::ROW_BYTES + ((((g % 2) * 2 + qq / 2) ^ swz_v<C>(vrow)) * 16) +
+                                    (qq % 2) * 8);
+  asm volatile("" : "+v"(kbase), "+v"(vbase));
   auto read = [&](int m) __attribute__((always_inline)) {
     bf16x8 a;
     if (m < NPV) {
       const int st = m / (D / 32), db = m % (D / 32);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int row = st * 16 + u * 8 + half * 4 + jr;
-        const int colb = (db * 32 + (g % 2) * 16 + qq * 4) * 2;  // byte offset in the row
-        const int ch = (colb / 16) ^ swz_v<C>(row);
-        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 LDS_AS*)(vl + row * C::ROW_BYTES + ch * 16 + (colb % 16)));
+        const uint32_t addr = (vbase ^ (uint32_t)(db * 64)) + (uint32_t)((st * 16 + u * 8) * C::ROW_BYTES);
+        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(uintptr_t)addr);
         const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
@@ -191,9 +246,8 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
     } else {
       const int mq = m - NPV;
       const int ks = mq / (BN / 32), kb = mq % (BN / 32);
-      const int row = kb * 32 + col;
-      const int ch = (2 * ks + half) ^ swz_k<C>(row);
-      a = *(const bf16x8 LDS_AS*)(kl + row * C::ROW_BYTES + ch * 16);
+      const uint32_t addr = (kbase ^ (uint32_t)(ks * 32)) + (uint32_t)(kb * 32 * C::ROW_BYTES);
+      a = *(const bf16x8 LDS_AS*)(uintptr_t)addr;
     }
     return a;
   };
@@ -207,6 +261,10 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
     if (m < NPV) {
       const int st = m / (D / 32), db = m % (D / 32);
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
+      if (rowsum_on_mfma(D) && db == D / 32 - 1) {
+        const f32x4 zero4 = {};
+        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[st], st == 0 ? zero4 : lsum, 0, 0, 0);
+      }
     } else {
       const int mq = m - NPV;
       const int ks = mq / (BN / 32), kb = mq % (BN / 32);
@@ -253,9 +311,13 @@ __device__ __forceinline__ float row_extreme(const f32x16 (&s)[BN / 32]) {
 }
 
 // P = exp2(S*c - m) rounded to bf16 and packed as the B operands of the P x V
-// MFMA (operand i covers keys 16 i .. 16 i + 15 of the tile).  Returns this
-// lane's sum of the rounded values over the tile (four independent chains).
-template <int BN>
+// MFMA (operand i covers keys 16 i .. 16 i + 15 of the tile).  Two VALU
+// operations per score (fma, exp) plus one conversion per pair.  With
+// VALU_SUM, also returns this lane's sum of the rounded values over the tile
+// (its 16 keys of each 32; four independent chains of two-element dot
+// products); otherwise the row sums are formed on the matrix core in the next
+// MFMA phase and 0 is returned.
+template <int BN, bool VALU_SUM>
 __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, float m_use,
                                            bf16x8 (&pb)[BN / 16]) {
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
@@ -268,10 +330,12 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8)
         p[t8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][sp * 8 + t8], c, -m_use));
+      if (VALU_SUM) {
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
-        const bf16x2 pp = {p[2 * t2], p[2 * t2 + 1]};
-        l4[t2] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l4[t2], false);
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const bf16x2 pp = {p[2 * t2], p[2 * t2 + 1]};
+          l4[t2] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l4[t2], false);
+        }
       }
       pb[kb * 2 + sp] = p;
     }
@@ -283,7 +347,7 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // ----------------------------------------------------------------------------
 template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WG_PER_CU, bool KEYS_SNAKE, bool CAUSAL,
           bool NEG_SCALE>
-__global__ __launch_bounds__(64 * WAVES, 2)
+__global__ __launch_bounds__(64 * WAVES, 2 * WG_PER_CU)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                           const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
@@ -331,6 +395,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const int q0 = qt * C::BM;
   int kend = L;
   if (CAUSAL) kend = min(kend, min(N, q0 + C::BM));
+  kend = __builtin_amdgcn_readfirstlane(kend);
   const int ntiles = (kend + BN - 1) / BN;
   // Key order (online softmax does not depend on it).  Causal query tiles of
   // a head run on one XCD longest first, RESIDENT at a time; call each such
@@ -353,29 +418,51 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // starting at wave W0 (each issues TILE_BYTES / (1 KiB * NW) loads).  Load i
   // of a lane fills LDS bytes pos = (i*64*NW + 64*(wave-W0) + lane)*16 of the
   // tile, i.e. row pos / ROW_BYTES and physical chunk (pos % ROW_BYTES) / 16;
-  // the lane fetches the logical chunk that the swizzle stores there.  A tail
-  // tile clamps rows >= kend to kend - 1 (masked keys: they only need to be
-  // finite memory inside the tensor; keys >= kv_len are never read).
+  // the lane fetches the logical chunk that the swizzle stores there.  Load i
+  // covers the rows of load 0 moved down by i * RSTEP, a multiple of the
+  // swizzle period, so its global offset is load 0's plus i * 16 * 64 * NW:
+  // on full tiles that step goes into the scalar base and one VGPR offset per
+  // lane serves every load.  A tail tile clamps rows >= kend to kend - 1
+  // (masked keys: they only need to be finite memory inside the tensor; keys
+  // >= kv_len are never read).
   auto issue = [&](auto nw_tag, int w0, const char* gsrc, bool is_v, int t, uint32_t dst)
       __attribute__((always_inline)) {
     constexpr int NW = decltype(nw_tag)::value;
     constexpr int TH = 64 * NW;
     constexpr int NLOADS = C::TILE_BYTES / 16 / TH;
+    constexpr int RSTEP = TH * 16 / C::ROW_BYTES;  // rows between loads i and i + 1
     static_assert(C::TILE_BYTES % (16 * TH) == 0, "tile must split evenly over the issuing waves");
+    static_assert((TH * 16) % C::ROW_BYTES == 0 && RSTEP % 16 == 0,
+                  "loads must step by whole rows and whole swizzle periods");
     const int j0 = ktile(t) * BN;
     const char* gt = gsrc + (size_t)j0 * C::ROW_BYTES;
-    const int last = kend - 1 - j0;  // last valid row of this tile
+    int last = kend - 1 - j0;  // last valid row of this tile
     const int wl = wave - w0;
+    const int pos0 = (wl * 64 + lane) * 16;
+    const int row0 = pos0 / C::ROW_BYTES;
+    const int lch = ((pos0 % C::ROW_BYTES) / 16) ^ (is_v ? swz_v<C>(row0) : swz_k<C>(row0));
+    const uint32_t l0 = lds_base + dst + (uint32_t)(wl * 64 * 16);
+    if (last >= BN - 1) {
+      uint32_t o = (uint32_t)(row0 * C::ROW_BYTES + lch * 16);
+      asm volatile("" : "+v"(o));  // one live offset; each load adds its step
 #pragma unroll
-    for (int i = 0; i < NLOADS; ++i) {
-      const int pos = (i * TH + wl * 64 + lane) * 16;
-      const int row = pos / C::ROW_BYTES;
-      const int pch = (pos % C::ROW_BYTES) / 16;
-      const int lch = pch ^ (is_v ? swz_v<C>(row) : swz_k<C>(row));
-      const int grow = row < last ? row : last;
-      const uint32_t o = (uint32_t)(grow * C::ROW_BYTES + lch * 16);
-      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_base + dst + (uint32_t)((i * TH + wl * 64) * 16));
-      dma16(gt, o, l);
+      for (int i = 0; i < NLOADS; ++i)
+        dma16(gt, o + (uint32_t)(i * TH * 16), __builtin_amdgcn_readfirstlane(l0 + (uint32_t)(i * TH * 16)));
+    } else {
+      // hide `last` (loop-invariant for the one tail tile) and the lane's row
+      // and chunk so that the clamped offsets are formed here rather than
+      // kept live across the key loop
+      last = __builtin_amdgcn_readfirstlane(last);
+      int r0 = row0, c16 = lch * 16;
+      asm volatile("" : "+s"(last), "+v"(r0), "+v"(c16));
+#pragma unroll
+      for (int i = 0; i < NLOADS; ++i) {
+        // min(row0 + i*RSTEP, last) = min(row0, last - i*RSTEP) + i*RSTEP
+        const int lim = last - i * RSTEP;
+        const int grow = r0 < lim ? r0 : lim;
+        const uint32_t o = (uint32_t)(grow * C::ROW_BYTES + c16) + (uint32_t)(i * TH * 16);
+        dma16(gt, o, __builtin_amdgcn_readfirstlane(l0 + (uint32_t)(i * TH * 16)));
+      }
     }
   };
   const int qrow = q0 + wave * 32 + col;  // the query row this lane owns
@@ -400,14 +487,23 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
 
-  f32x16 acc[D / 32];
+  // Selection operand of the row-sum MFMA (see mfma_stream): lane 16g + i
+  // holds row i, k-group g of a 16 x 32 matrix that is 1 on rows 0 and 8 for
+  // even g and on rows 4 and 12 for odd g.
+  bf16x8 sel;
+  {
+    const int i = lane % 16, g = lane / 16;
+    const bool one = (g % 2 == 0) ? (i == 0 || i == 8) : (i == 4 || i == 12);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    for (int e = 0; e < 8; ++e) sel[e] = (__bf16)(one ? 1.f : 0.f);
+  }
 
-  float m_run = -INFINITY;  // running shift, exp2 domain (scores * c)
-  float l_run = 0.f;        // this lane's partial row sum (its 16 keys of each 32)
+  constexpr bool RS_MFMA = rowsum_on_mfma(D);
+  f32x16 acc[D / 32];
+  float m_run;   // running shift, exp2 domain (scores * c)
+  float l_run;   // row sum of this lane's query: whole (RS_MFMA), else its 16 keys of each 32
+  f32x4 lsum;    // element 0: this query's sum of the last tile's P (matrix core)
+  bool bad;      // a tile's row sum was not finite: some probability overflowed
 
   f32x16 s0[BN / 32];
   bf16x8 pb[BN / 16];
@@ -427,61 +523,112 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       l_run *= alpha;
     }
   };
-  // VALU part of tile t: mask, P(t), row sums.  The shift is computed on the
-  // first tile that shows a row a visible key and afterwards only when this
-  // tile's row sum shows that some probability would exceed 2^16 (or is not
-  // finite); any shift at or below the row maximum gives the same softmax, so
-  // the result is exact up to rounding and every probability stays within
-  // [0, 2^16].
-  auto softmax_tile = [&](int t) __attribute__((always_inline)) {
-    if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0, ktile(t) * BN, L, qrow, half);
-    // rows without a shift yet (no visible key so far) also take this tile's
-    // maxima: on the first tile the fast path is computed and then redone
-    float lt = softmax_p<BN>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
-    if (__builtin_amdgcn_ballot_w64(!(lt <= kLazySumMax) || m_run == -INFINITY) != 0) {
-      update_shift();
-      lt = softmax_p<BN>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+  // Fold in the row sums of the previous tile, which the MFMA phase just
+  // formed together with its P x V.  The shift is lazy: it is taken from the
+  // first tile that shows a row a visible key and afterwards moved only when a
+  // tile's row sum shows a probability above 2^16, by the integer part of that
+  // sum's log2 (an exact power-of-two rescale of acc and l).  Any shift gives
+  // the same softmax (it cancels between numerator and denominator), so the
+  // result is exact up to rounding.  The test comes one tile late, after the
+  // tile's P x V: a sum that is not finite means some exp2 overflowed, and the
+  // workgroup then recomputes its rows with the shift checked before every
+  // tile (the safe pass below).
+  auto fold_sum = [&]() __attribute__((always_inline)) {
+    const float rs = lsum[0];
+    bad = bad || !(rs <= FLT_MAX);
+    if (__builtin_amdgcn_ballot_w64(rs > kLazySumMax) != 0) {
+      const float mv = (rs > kLazySumMax && rs <= FLT_MAX) ? floorf(__builtin_amdgcn_logf(rs)) : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-mv);
+      m_run += mv;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      l_run = (l_run + rs) * alpha;
+    } else {
+      l_run += rs;
     }
-    l_run += lt;
   };
+  // VALU part of tile t: fold the previous tile's row sums, mask, shift (first
+  // visible tile, or every tile in the safe pass), P(t).
+  // With the VALU row sum the test needs no deferral: the tile's sum is known
+  // before its P x V, and a tile whose sum exceeds 2^16 (or is not finite) is
+  // recomputed after moving the shift to the tile's row maxima.
+  auto softmax_tile = [&](int t, auto safe_tag) __attribute__((always_inline)) {
+    constexpr bool SAFE = decltype(safe_tag)::value;
+    if (RS_MFMA) fold_sum();
+    if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0, ktile(t) * BN, L, qrow, half);
+    if (RS_MFMA) {
+      if (SAFE || __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) update_shift();
+      softmax_p<BN, false>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+    } else {
+      float lt = softmax_p<BN, true>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+      if (__builtin_amdgcn_ballot_w64(!(lt <= kLazySumMax) || m_run == -INFINITY) != 0) {
+        update_shift();
+        lt = softmax_p<BN, true>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+      }
+      l_run += lt;
+    }
+  };
+
+  // One pass over the keys.  The safe pass is a second, straight-line copy
+  // (a loop around one copy would carry every accumulator across its back
+  // edge and push the register count past the two-waves-per-SIMD limit).
+  auto run_pass = [&](auto safe_tag) __attribute__((always_inline)) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  m_run = -INFINITY;
+  l_run = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lsum[r] = 0.f;
+  bad = false;
 
   if (PINGPONG) {
     // Ping-pong.  The waves split into two groups of WAVES/2; waves w and
     // w + WAVES/2 share a SIMD.  Every wave runs the same straight loop
     // MFMA(t), barrier, VALU(t), barrier, with
-    //   MFMA(t) = O += V(t-1)^T P(t-1)^T (t >= 1), then S(t) = K(t) Q^T (t < ntiles)
+    //   MFMA(t) = O += V(t-1)^T P(t-1)^T and row sums of P(t-1) (t >= 1),
+    //             then S(t) = K(t) Q^T (t < ntiles)
     //   VALU(t) = softmax of tile t;
     // group 1 passes one extra barrier first, which shifts it half a tile
     // behind group 0 (a barrier counts arrivals, not program locations), so on
     // each SIMD one group's MFMA stream runs under the other's softmax.  The
     // MFMA phase runs at raised wave priority.  K and V tiles have two LDS
     // buffers each.  Global half-step h = 2t starts group 0's MFMA(t) and
-    // group 1's VALU(t-1); there group 1 issues the DMAs of K(t+1) and V(t)
-    // (its softmax has slack, group 0's MFMA stream has none) and waits for
-    // them at the end of h = 2t + 1, before the barrier that publishes them.
+    // group 1's VALU(t-1); there group 1 issues the DMA of K(t+1) and waits
+    // for it at the end of h = 2t + 1.  Group 0 issues the DMA of V(t) at the
+    // start of its VALU(t) (h = 2t + 1: V(t-2)'s buffer was last read in
+    // h = 2t - 1) and waits for it at the end of that half step.  The DMAs are
+    // issued by softmax waves only (a wave stalls while the CU's load path
+    // drains its DMAs, which the MFMA stream cannot absorb), and split over
+    // both groups so that each softmax half step carries half of them.
     const int grp = wave / (WAVES / 2);  // wave-uniform
     auto kd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t & 1) * C::TILE_BYTES); };
     auto vd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((2 + (t & 1)) * C::TILE_BYTES); };
-    std::integral_constant<int, WAVES / 2> g1_tag;
+    std::integral_constant<int, WAVES / 2> half_tag;
     std::integral_constant<int, WAVES> all_tag;
+    // group 1's DMA at its VALU(t - 1): K(t + 1)
     auto issue_step = [&](int t) __attribute__((always_inline)) {
-      if (t + 1 < ntiles) issue(g1_tag, WAVES / 2, Kg, false, t + 1, kd(t + 1));
-      if (t < ntiles) issue(g1_tag, WAVES / 2, Vg, true, t, vd(t));
+      if (t + 1 < ntiles) issue(half_tag, WAVES / 2, Kg, false, t + 1, kd(t + 1));
     };
     // one half-step pair of tile t; `mf` is the MFMA phase
-    auto step = [&](int t, auto&& mf) __attribute__((always_inline)) {
+    auto step = [&](int t, auto st_tag, auto&& mf) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(2);
       mf();
       __builtin_amdgcn_s_setprio(0);
       if (grp == 1) wait_dma();
       __syncthreads();
       if (grp == 1) issue_step(t + 1);
-      softmax_tile(t);
+      else issue(half_tag, 0, Vg, true, t, vd(t));
+      softmax_tile(t, st_tag);
       // keep the softmax in this half step: without these uses the compiler
       // sinks the exponentials past the barrier, next to the P x V MFMAs
 #pragma unroll
       for (int i = 0; i < BN / 16; ++i) asm volatile("" ::"v"(pb[i]));
       asm volatile("" ::"v"(l_run));
+      if (grp == 0) wait_dma();
       __syncthreads();
     };
     if (ntiles > 0) {
@@ -492,16 +639,18 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         issue_step(0);
         __syncthreads();
       }
-      step(0, [&]() __attribute__((always_inline)) {
-        mfma_stream<C, D, BN, false, true>(smem, pb, acc, smem + kd(0), qf, s0, lane);
+      step(0, safe_tag, [&]() __attribute__((always_inline)) {
+        mfma_stream<C, D, BN, false, true>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
       });
       for (int t = 1; t < ntiles; ++t)
-        step(t, [&]() __attribute__((always_inline)) {
-          mfma_stream<C, D, BN, true, true>(smem + vd(t - 1), pb, acc, smem + kd(t), qf, s0, lane);
+        step(t, safe_tag, [&]() __attribute__((always_inline)) {
+          mfma_stream<C, D, BN, true, true>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t), qf, s0,
+                                            lane);
         });
       __builtin_amdgcn_s_setprio(2);
-      mfma_stream<C, D, BN, true, false>(smem + vd(ntiles - 1), pb, acc, smem, qf, s0, lane);
+      mfma_stream<C, D, BN, true, false>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem, qf, s0, lane);
       __builtin_amdgcn_s_setprio(0);
+      if (RS_MFMA) fold_sum();
       if (grp == 0) __syncthreads();  // group 1's last VALU barrier
     }
   } else {
@@ -526,20 +675,36 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         issue(all_tag, 0, Kg, false, t + AHEAD, sk(t + AHEAD));
         issue(all_tag, 0, Vg, true, t + AHEAD, sv(t + AHEAD));
       }
-      mfma_stream<C, D, BN, false, true>(smem, pb, acc, smem + sk(t), qf, s0, lane);
-      softmax_tile(t);
-      mfma_stream<C, D, BN, true, false>(smem + sv(t), pb, acc, smem, qf, s0, lane);
+      mfma_stream<C, D, BN, false, true>(smem, pb, acc, sel, lsum, smem + sk(t), qf, s0, lane);
+      softmax_tile(t, safe_tag);
+      mfma_stream<C, D, BN, true, false>(smem + sv(t), pb, acc, sel, lsum, smem, qf, s0, lane);
       // tile t + 1 must have landed; the DMAs of tiles t + 2 .. t + AHEAD may
       // stay in flight (2 * LOADS instructions per tile and wave)
       if (more) wait_dma_n<(AHEAD - 1) * 2 * LOADS>();
       else wait_dma();
       __syncthreads();
     }
+    if (RS_MFMA) fold_sum();
+  }
+  };
+  // The fast pass; then a workgroup vote.  Every wave has finished the pass
+  // (no DMA is in flight and no LDS tile is read after the barrier), so the
+  // safe pass can reuse the ring.
+  int LDS_AS* vote = (int LDS_AS*)(smem + C::LDS_BYTES);
+  if (tid == 0) *vote = 0;
+  run_pass(std::false_type{});
+  if (RS_MFMA) {  // the VALU row sum tests every tile before its P x V
+    if (bad) *vote = 1;
+    __syncthreads();
+    if (*vote != 0) run_pass(std::true_type{});
   }
 
   // ---------------- epilogue: O = O^T / l ----------------
-  const u32x2 lp = swap_halves(l_run);
-  const float l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
+  float l_tot = l_run;
+  if (!RS_MFMA) {
+    const u32x2 lp = swap_halves(l_run);
+    l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // log-sum-exp: sum_j 2^(c s_j) = 2^m_run * l, so ln(sum_j e^(scale s_j)) = (m_run + log2 l) ln 2
   if (lse != nullptr && half == 0 && qrow < N)
@@ -571,7 +736,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   float c = a.scale * kLog2e;
   if (c == 0.f) c = FLT_MIN;
   auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, STAGES, PINGPONG, WPC, SNAKE, CAUSAL, NEG>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES + 16, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
                      a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
@@ -605,11 +770,15 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t stream) {
 #ifndef ATTNIO_STAGES
 #define ATTNIO_STAGES 2
 #endif
-// WG_PER_CU: workgroups resident per CU, used by the host I/O model.  It
-// follows from the compiled register counts (d = 128: 249 VGPRs, 2 waves per
-// SIMD, so one 8-wave workgroup per CU, which also fills 128 KiB of LDS;
-// d = 64: 127 VGPRs, 4 waves per SIMD, two workgroups of 32 KiB LDS each).
+// WG_PER_CU: workgroups resident per CU.  The kernel asks the compiler for
+// 2 * WG_PER_CU waves per SIMD (the register budget: 256 VGPRs for one 8-wave
+// workgroup per CU, 128 for two), and the causal key order and the host I/O
+// model assume that residency (d = 128: one workgroup, 128 KiB of LDS;
+// d = 64: WG_PER_CU workgroups of 32 KiB LDS each).
 // KEYS_SNAKE: causal generations alternate the key direction (see the kernel).
+#ifndef ATTNIO_WPC_D64
+#define ATTNIO_WPC_D64 2
+#endif
 #ifndef ATTNIO_SNAKE_D128
 #define ATTNIO_SNAKE_D128 1
 #endif
@@ -628,7 +797,7 @@ template <> struct Pick<64> {
   static constexpr int D = 64, BN = ATTNIO_BN_D64, WAVES = ATTNIO_PINGPONG ? 8 : 4;
   static constexpr int STAGES = ATTNIO_STAGES;
   static constexpr bool PINGPONG = ATTNIO_PINGPONG != 0;
-  static constexpr int WG_PER_CU = ATTNIO_PINGPONG ? 2 : 4;
+  static constexpr int WG_PER_CU = ATTNIO_PINGPONG ? ATTNIO_WPC_D64 : 4;
   static constexpr bool KEYS_SNAKE = ATTNIO_SNAKE_D64 != 0;
 };
 

@@ -3,7 +3,8 @@
 Closed forms and invariants of the definition (constant values, zero scale,
 masked keys contributing nothing, fully masked rows), run-to-run determinism,
 stream ordering, a negative scale, an input that forces the running maximum to
-grow on every key tile, and the largest supported tensor size.
+grow on every key tile, an input whose probabilities overflow the first
+tile's exponent shift, and the largest supported tensor size.
 """
 
 import math
@@ -129,6 +130,36 @@ def test_running_max_grows_every_tile():
         out = run_gpu(q, k, v, causal, None, 1.0, "bf16")
         want = oracle_rows(q, k, v, causal, None, 1.0, "bf16")
         compare(gpu_rows(out), want, "bf16", f"ramp causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_overflow_recomputed(d, causal):
+    """Keys 300.. score about 128 (x log2 e = 185 in the exponent) above the
+    first key tile on every even row, so the exponent shift taken from that
+    tile overflows exp2 there; odd rows stay small.  With the row sum formed
+    after the P x V (d = 128) the overflow is seen one tile late and the
+    workgroup recomputes its rows with the shift checked before every tile;
+    with the row sum formed before it (d = 64) the tile is recomputed at once.
+    Either way O must match the oracle on every row, overflowing or not."""
+    N = 1000
+    _log(f"overflow d={d} causal={causal}")
+    g = torch.Generator().manual_seed(39)
+    qs, ks = [], []
+    for h in range(2):
+        u = torch.randn(d, generator=g)
+        u = u / u.norm() * 4.0
+        t = 0.1 * torch.randn(N, generator=g)
+        t[300:] += 8.0
+        s = torch.where(torch.arange(N) % 2 == 0, 1.0, 0.05)
+        qs.append(s[:, None] * u[None, :])
+        ks.append(t[:, None] * u[None, :])
+    q = torch.stack(qs)[None].to(torch.bfloat16).contiguous()
+    k = torch.stack(ks)[None].to(torch.bfloat16).contiguous()
+    v = torch.randn(1, 2, N, d, generator=g).to(torch.bfloat16)
+    out = run_gpu(q, k, v, causal, None, 1.0, "bf16")
+    want = oracle_rows(q, k, v, causal, None, 1.0, "bf16")
+    compare(gpu_rows(out), want, "bf16", f"overflow d={d} causal={causal}")
 
 
 def test_non_default_stream_ordering():
