@@ -168,12 +168,14 @@ __device__ __forceinline__ void wait_dma_n() {
 // lone 32x32x16 chain at its full rate of one MFMA per 32 cycles even with
 // 1 KiB of LDS reads per MFMA, while reading 1-2 ahead (what the compiler
 // schedules on its own) costs about 40%.
-constexpr int kReadAhead = 4;
+#ifndef ATTNIO_READ_AHEAD
+#define ATTNIO_READ_AHEAD 4
+#endif
+constexpr int kReadAhead = ATTNIO_READ_AHEAD;
 
 // One MFMA phase as a single stream of MFMAs:
 //   DO_PV: O^T (D x 32 queries) += V_tile^T P^T   ((BN/16) x (D/32) MFMAs)
-//          and, when formed there, the tile's row sums of P
-//                                                  (BN/16 MFMAs, 16x16x32)
+//          and, with DO_RS, the tile's row sums of P (BN/16 MFMAs, 16x16x32)
 //   DO_QK: S^T (BN keys x 32 queries) = K_tile Q^T ((D/16) x (BN/32) MFMAs)
 // in that order.  Each group of D/32 (resp. BN/32) consecutive MFMAs writes
 // independent accumulators, so dependent MFMAs are at least 3 apart.
@@ -198,7 +200,7 @@ constexpr int kReadAhead = 4;
 // same keys, so P needs no register shuffle.  The K operand is one 16-byte
 // read of row kb*32 + c.  A scheduling barrier after every MFMA pins the
 // read-ahead distance.
-template <class C, int D, int BN, bool DO_PV, bool DO_QK>
+template <class C, int D, int BN, bool DO_PV, bool DO_QK, bool DO_RS>
 __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 (&pb)[BN / 16],
                                             f32x16 (&acc)[D / 32], const bf16x8& sel, f32x4& lsum,
                                             const char LDS_AS* kl, const bf16x8 (&qf)[D / 16],
@@ -230,7 +232,10 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
   uint32_t vbase = (uint32_t)(uintptr_t)vl +
                          (uint32_t)(vrow * C::ROW_BYTES + ((((g % 2) * 2 + qq / 2) ^ swz_v<C>(vrow)) * 16) +
                                     (qq % 2) * 8);
-  asm volatile("" : "+v"(kbase), "+v"(vbase));
+#ifndef ATTNIO_ADDR_REMAT
+#define ATTNIO_ADDR_REMAT 1
+#endif
+  if (ATTNIO_ADDR_REMAT) asm volatile("" : "+v"(kbase), "+v"(vbase));
   auto read = [&](int m) __attribute__((always_inline)) {
     bf16x8 a;
     if (m < NPV) {
@@ -261,7 +266,7 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
     if (m < NPV) {
       const int st = m / (D / 32), db = m % (D / 32);
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
-      if (rowsum_on_mfma(D) && db == D / 32 - 1) {
+      if (DO_RS && db == D / 32 - 1) {
         const f32x4 zero4 = {};
         lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[st], st == 0 ? zero4 : lsum, 0, 0, 0);
       }
@@ -347,7 +352,7 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // ----------------------------------------------------------------------------
 template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WG_PER_CU, bool KEYS_SNAKE, bool CAUSAL,
           bool NEG_SCALE>
-__global__ __launch_bounds__(64 * WAVES, 2 * WG_PER_CU)
+__global__ __launch_bounds__(64 * WAVES, (WAVES / 4) * WG_PER_CU)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                           const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
@@ -499,6 +504,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   }
 
   constexpr bool RS_MFMA = rowsum_on_mfma(D);
+  // Ping-pong: the softmax wave issues the row-sum MFMAs of its previous P at
+  // the start of its half step, while the MFMA wave of the SIMD waits for the
+  // first LDS operands of the freshly published tiles (the matrix pipe is
+  // otherwise idle there); the sequential form keeps them in the P x V stream.
+  constexpr bool RS_STREAM = RS_MFMA && !PINGPONG;
   f32x16 acc[D / 32];
   float m_run;   // running shift, exp2 domain (scores * c)
   float l_run;   // row sum of this lane's query: whole (RS_MFMA), else its 16 keys of each 32
@@ -508,11 +518,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   f32x16 s0[BN / 32];
   bf16x8 pb[BN / 16];
 
-  // Move the shift to the current row extremes of s0 where some row's extreme
-  // exceeds it by more than 2^TAU, rescaling acc and l (wave-uniform branch).
+  // Move the shift to the current row extremes of s0 where a row's extreme
+  // exceeds it by more than 2^TAU, rescaling acc and l.  The rescales here and
+  // in fold_sum are per-lane branches (executed under the lane mask, skipped
+  // when no lane needs them): as wave-uniform branches the compiler gave the
+  // two paths different accumulator registers and copied all 64 of them on
+  // the common path of every tile.
   auto update_shift = [&]() __attribute__((always_inline)) {
     const float m_tile = row_extreme<BN, NEG_SCALE>(s0) * c;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kTauLog2) != 0) {
+    if (m_tile > m_run + kTauLog2) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -523,8 +537,14 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       l_run *= alpha;
     }
   };
-  // Fold in the row sums of the previous tile, which the MFMA phase just
-  // formed together with its P x V.  The shift is lazy: it is taken from the
+  // Row sums of the P held in pb (16x16x32 MFMAs with the selection operand).
+  auto rowsum_mfma = [&]() __attribute__((always_inline)) {
+    const f32x4 zero4 = {};
+#pragma unroll
+    for (int st = 0; st < BN / 16; ++st)
+      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[st], st == 0 ? zero4 : lsum, 0, 0, 0);
+  };
+  // Fold in the row sums of the previous tile (formed after its P x V).  The shift is lazy: it is taken from the
   // first tile that shows a row a visible key and afterwards moved only when a
   // tile's row sum shows a probability above 2^16, by the integer part of that
   // sum's log2 (an exact power-of-two rescale of acc and l).  Any shift gives
@@ -536,17 +556,16 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   auto fold_sum = [&]() __attribute__((always_inline)) {
     const float rs = lsum[0];
     bad = bad || !(rs <= FLT_MAX);
-    if (__builtin_amdgcn_ballot_w64(rs > kLazySumMax) != 0) {
-      const float mv = (rs > kLazySumMax && rs <= FLT_MAX) ? floorf(__builtin_amdgcn_logf(rs)) : 0.f;
+    l_run += rs;
+    if (rs > kLazySumMax && rs <= FLT_MAX) {
+      const float mv = floorf(__builtin_amdgcn_logf(rs));
       const float alpha = __builtin_amdgcn_exp2f(-mv);
       m_run += mv;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l_run = (l_run + rs) * alpha;
-    } else {
-      l_run += rs;
+      l_run *= alpha;
     }
   };
   // VALU part of tile t: fold the previous tile's row sums, mask, shift (first
@@ -559,7 +578,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     if (RS_MFMA) fold_sum();
     if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0, ktile(t) * BN, L, qrow, half);
     if (RS_MFMA) {
-      if (SAFE || __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0) update_shift();
+      // per lane: the two lanes of a query (c, c + 32) share m_run, so the
+      // permlane32 swap in row_extreme only pairs active lanes
+      if (SAFE || m_run == -INFINITY) update_shift();
       softmax_p<BN, false>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
     } else {
       float lt = softmax_p<BN, true>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
@@ -585,13 +606,12 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   for (int r = 0; r < 4; ++r) lsum[r] = 0.f;
   bad = false;
 
-  if (PINGPONG) {
+  if constexpr (PINGPONG) {
     // Ping-pong.  The waves split into two groups of WAVES/2; waves w and
     // w + WAVES/2 share a SIMD.  Every wave runs the same straight loop
     // MFMA(t), barrier, VALU(t), barrier, with
-    //   MFMA(t) = O += V(t-1)^T P(t-1)^T and row sums of P(t-1) (t >= 1),
-    //             then S(t) = K(t) Q^T (t < ntiles)
-    //   VALU(t) = softmax of tile t;
+    //   MFMA(t) = O += V(t-1)^T P(t-1)^T (t >= 1), then S(t) = K(t) Q^T (t < ntiles)
+    //   VALU(t) = [d = 128: row sums of P(t-1) on the matrix core,] softmax of tile t;
     // group 1 passes one extra barrier first, which shifts it half a tile
     // behind group 0 (a barrier counts arrivals, not program locations), so on
     // each SIMD one group's MFMA stream runs under the other's softmax.  The
@@ -620,6 +640,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       __builtin_amdgcn_s_setprio(0);
       if (grp == 1) wait_dma();
       __syncthreads();
+      if (RS_MFMA && t > 0) rowsum_mfma();  // P(t - 1), still in pb
       if (grp == 1) issue_step(t + 1);
       else issue(half_tag, 0, Vg, true, t, vd(t));
       softmax_tile(t, st_tag);
@@ -640,17 +661,21 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         __syncthreads();
       }
       step(0, safe_tag, [&]() __attribute__((always_inline)) {
-        mfma_stream<C, D, BN, false, true>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
+        mfma_stream<C, D, BN, false, true, false>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
       });
       for (int t = 1; t < ntiles; ++t)
         step(t, safe_tag, [&]() __attribute__((always_inline)) {
-          mfma_stream<C, D, BN, true, true>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t), qf, s0,
-                                            lane);
+          mfma_stream<C, D, BN, true, true, false>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t), qf,
+                                                   s0, lane);
         });
       __builtin_amdgcn_s_setprio(2);
-      mfma_stream<C, D, BN, true, false>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem, qf, s0, lane);
+      mfma_stream<C, D, BN, true, false, false>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem, qf, s0,
+                                                lane);
       __builtin_amdgcn_s_setprio(0);
-      if (RS_MFMA) fold_sum();
+      if (RS_MFMA) {
+        rowsum_mfma();
+        fold_sum();
+      }
       if (grp == 0) __syncthreads();  // group 1's last VALU barrier
     }
   } else {
@@ -675,9 +700,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         issue(all_tag, 0, Kg, false, t + AHEAD, sk(t + AHEAD));
         issue(all_tag, 0, Vg, true, t + AHEAD, sv(t + AHEAD));
       }
-      mfma_stream<C, D, BN, false, true>(smem, pb, acc, sel, lsum, smem + sk(t), qf, s0, lane);
+      mfma_stream<C, D, BN, false, true, false>(smem, pb, acc, sel, lsum, smem + sk(t), qf, s0, lane);
       softmax_tile(t, safe_tag);
-      mfma_stream<C, D, BN, true, false>(smem + sv(t), pb, acc, sel, lsum, smem, qf, s0, lane);
+      mfma_stream<C, D, BN, true, false, RS_STREAM>(smem + sv(t), pb, acc, sel, lsum, smem, qf, s0, lane);
       // tile t + 1 must have landed; the DMAs of tiles t + 2 .. t + AHEAD may
       // stay in flight (2 * LOADS instructions per tile and wave)
       if (more) wait_dma_n<(AHEAD - 1) * 2 * LOADS>();
@@ -771,8 +796,8 @@ hipError_t dispatch_mask(const FwdArgs& a, hipStream_t stream) {
 #define ATTNIO_STAGES 2
 #endif
 // WG_PER_CU: workgroups resident per CU.  The kernel asks the compiler for
-// 2 * WG_PER_CU waves per SIMD (the register budget: 256 VGPRs for one 8-wave
-// workgroup per CU, 128 for two), and the causal key order and the host I/O
+// (WAVES / 4) * WG_PER_CU waves per SIMD (the register budget: 256 VGPRs for
+// one 8-wave workgroup per CU, 128 for two), and the causal key order and the host I/O
 // model assume that residency (d = 128: one workgroup, 128 KiB of LDS;
 // d = 64: WG_PER_CU workgroups of 32 KiB LDS each).
 // KEYS_SNAKE: causal generations alternate the key direction (see the kernel).
