@@ -74,6 +74,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -478,12 +479,17 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane (h, c) holds
   //      Q[qrow][16*ks + 8*h .. +7] for every ks ----
+  // Q is read once, so its loads are non-temporal: they do not push out of L2
+  // the K/V tiles that the other query tiles of the head on this XCD are about
+  // to read.  O, written once, leaves the same way from the epilogue (in whole
+  // lines: a non-temporal store of 8-byte pieces would leave L2 unable to
+  // merge them, measured at 4.8x the bytes written).
   bf16x8 qf[D / 16];
   {
     const int qrow_c = qrow < N ? qrow : N - 1;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = *(const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 16 + half * 8);
+      qf[ks] = __builtin_nontemporal_load((const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 16 + half * 8));
   }
   // Q operands must have arrived before the key loop: an empty asm that reads
   // them makes the compiler wait for their loads here, so that no wait for a
@@ -732,19 +738,40 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // log-sum-exp: sum_j 2^(c s_j) = 2^m_run * l, so ln(sum_j e^(scale s_j)) = (m_run + log2 l) ln 2
+  // (one 128-byte line per wave: the 32 lanes of half 0 write consecutive rows)
   if (lse != nullptr && half == 0 && qrow < N)
-    lse[(size_t)bh * N + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  if (qrow < N) {
-    __bf16* orow = Os + (size_t)qrow * D;
+    __builtin_nontemporal_store(l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY,
+                                lse + (size_t)bh * N + qrow);
+  // O leaves through LDS so that it can be written in whole lines with
+  // non-temporal stores (streamed past L2, where the K/V tiles of the head's
+  // other query tiles stay).  Lane (h, c) holds 4-element pieces of row c; it
+  // writes them into this wave's 32 x ROW_BYTES slice of the (now idle) ring,
+  // 16-byte chunks XOR-swizzled by the row (spreads the 32 rows' equal
+  // columns over the banks); then each store instruction of the wave writes
+  // 1 KiB of whole rows, 16 contiguous bytes per lane.
+  __syncthreads();  // every wave is past its last read of the K/V ring
+  static_assert(32 * C::ROW_BYTES * WAVES <= C::LDS_BYTES, "output staging must fit the ring");
+  char LDS_AS* ost = smem + wave * 32 * C::ROW_BYTES;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        bf16x4 o;
+    for (int a4 = 0; a4 < 4; ++a4) {
+      bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[db][a4 * 4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + a4 * 8 + half * 4) = o;
-      }
+      for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[db][a4 * 4 + e] * inv);
+      const int byte = (db * 32 + a4 * 8 + half * 4) * 2;  // within row c
+      const int ch = (byte / 16) ^ (col % C::CHUNKS);
+      *(bf16x4 LDS_AS*)(ost + col * C::ROW_BYTES + ch * 16 + byte % 16) = o;
+    }
+  constexpr int ROWS_PER_STORE = 64 / C::CHUNKS;  // rows one 64-lane store covers
+  const int q_w = q0 + wave * 32;                 // first query row of this wave
+#pragma unroll
+  for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
+    const int row = i * ROWS_PER_STORE + lane / C::CHUNKS;
+    const int chunk = lane % C::CHUNKS;
+    const u32x4 v = *(const u32x4 LDS_AS*)(ost + row * C::ROW_BYTES + ((chunk ^ (row % C::CHUNKS)) * 16));
+    if (q_w + row < N)
+      __builtin_nontemporal_store(v, (u32x4*)(Os + (size_t)(q_w + row) * D + chunk * 8));
   }
 }
 
