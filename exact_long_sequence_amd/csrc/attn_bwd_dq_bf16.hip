@@ -291,22 +291,31 @@ void attn_bwd_dq_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restric
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // VALU phase of tile t: dS^T = P^T (dP^T - D) as B operands (masking as in
-    // the kernel above: one compare of a constant with tk per score)
+    // VALU phase of tile t: dS^T = P^T (dP^T - D) as B operands.  Only tiles
+    // that reach past some lane's last visible key (the diagonal, the kv_len
+    // tail) test each score (one compare of a constant with tk, as in the
+    // kernel above); the wave-uniform test per tile drops the compare and the
+    // select from the others (two of the 6.5 VALU operations per score).
+    const int wave_last = __builtin_amdgcn_readfirstlane(CAUSAL ? min(L - 1, q0 + wave * 32) : L - 1);
     auto valu_phase = [&](int t) __attribute__((always_inline)) {
       const int tk = last - t * BN - half * 4;
+      auto body = [&](auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
+          for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
-          for (int t8 = 0; t8 < 8; ++t8) {
-            const int r = sp * 8 + t8;
-            const float arg = (kb * 32 + (r / 4) * 8 + (r % 4) <= tk)
-                                  ? __builtin_fmaf(s[kb][r], c, -lse2) : -INFINITY;
-            const float p = __builtin_amdgcn_exp2f(arg);
-            pds[kb * 2 + sp][t8] = (__bf16)(p * (dp[kb][r] - dlt));
-          }
+            for (int t8 = 0; t8 < 8; ++t8) {
+              const int r = sp * 8 + t8;
+              const float arg = (!MASKED || kb * 32 + (r / 4) * 8 + (r % 4) <= tk)
+                                    ? __builtin_fmaf(s[kb][r], c, -lse2) : -INFINITY;
+              const float p = __builtin_amdgcn_exp2f(arg);
+              pds[kb * 2 + sp][t8] = (__bf16)(p * (dp[kb][r] - dlt));
+            }
+      };
+      if (t * BN + BN - 1 > wave_last) body(std::true_type{});
+      else body(std::false_type{});
     };
     // prologue: K(0), V(0) by all waves; group 1 issues K(1) and passes one
     // extra barrier, which puts it half a tile behind group 0
