@@ -285,8 +285,10 @@ void attn_bwd_dq_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restric
         } else {
           const int mq = m - NDQ, ks = mq / (2 * (BN / 32)), kb = (mq / 2) % (BN / 32);
           const f32x16 zero = {};
-          if (mq % 2) dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dof[ks], ks == 0 ? zero : dp[kb], 0, 0, 0);
-          else s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[kb], 0, 0, 0);
+          if (mq % 2)
+            dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dof[ks], ks == 0 ? zero : dp[kb], 0, 0, 0);
+          else
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[kb], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -335,9 +337,11 @@ void attn_bwd_dq_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restric
       if (grp == 1) wait_dma();
       __syncthreads();
       if (grp == 1) {
-        if (t + 2 < ntiles) dma_rows<D, BN, 256>(Ks, (t + 2) * BN, kend - 1, lds_base + kbuf(t + 2), wl, lane);
+        if (t + 2 < ntiles)
+          dma_rows<D, BN, 256>(Ks, (t + 2) * BN, kend - 1, lds_base + kbuf(t + 2), wl, lane);
       } else {
-        if (t + 1 < ntiles) dma_rows<D, BN, 256>(Vs, (t + 1) * BN, kend - 1, lds_base + vbuf(t + 1), wl, lane);
+        if (t + 1 < ntiles)
+          dma_rows<D, BN, 256>(Vs, (t + 1) * BN, kend - 1, lds_base + vbuf(t + 1), wl, lane);
       }
       valu_phase(t);
       // keep the VALU work in this half step (its only use is the next dQ MFMAs)

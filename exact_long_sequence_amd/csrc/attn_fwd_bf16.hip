@@ -81,7 +81,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTauLog2 = 8.0f;        // shift moves when a row maximum exceeds it by 2^8
-constexpr float kLazySumMax = 65536.f;  // a tile row sum above this recomputes the shift
+constexpr float kLazySumMax = 65536.f;  // a tile row sum above this moves the shift
 
 // Where the row sums of P are formed: on the matrix core (next to the P x V
 // MFMAs, one tile late) or on the VALU (two-element dot products, in the
@@ -550,10 +550,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     for (int st = 0; st < BN / 16; ++st)
       lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[st], st == 0 ? zero4 : lsum, 0, 0, 0);
   };
-  // Fold in the row sums of the previous tile (formed after its P x V).  The shift is lazy: it is taken from the
-  // first tile that shows a row a visible key and afterwards moved only when a
-  // tile's row sum shows a probability above 2^16, by the integer part of that
-  // sum's log2 (an exact power-of-two rescale of acc and l).  Any shift gives
+  // Fold in the row sums of the previous tile (formed after its P x V).  The
+  // shift is lazy: it is taken from the first tile that shows a row a visible
+  // key and afterwards moved only when a tile's row sum shows a probability
+  // above 2^16, by the integer part of that sum's log2 (an exact power-of-two
+  // rescale of acc and l).  Any shift gives
   // the same softmax (it cancels between numerator and denominator), so the
   // result is exact up to rounding.  The test comes one tile late, after the
   // tile's P x V: a sum that is not finite means some exp2 overflowed, and the
