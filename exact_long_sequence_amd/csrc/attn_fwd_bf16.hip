@@ -554,12 +554,12 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // shift is lazy: it is taken from the first tile that shows a row a visible
   // key and afterwards moved only when a tile's row sum shows a probability
   // above 2^16, by the integer part of that sum's log2 (an exact power-of-two
-  // rescale of acc and l).  Any shift gives
-  // the same softmax (it cancels between numerator and denominator), so the
-  // result is exact up to rounding.  The test comes one tile late, after the
-  // tile's P x V: a sum that is not finite means some exp2 overflowed, and the
-  // workgroup then recomputes its rows with the shift checked before every
-  // tile (the safe pass below).
+  // rescale of acc and l).  Any shift gives the same softmax (it cancels
+  // between numerator and denominator), so the result is exact up to
+  // rounding.  The test comes one tile late, after the tile's P x V: a sum
+  // that is not finite means some exp2 overflowed, and the workgroup then
+  // recomputes its rows with the shift checked before every tile (the safe
+  // pass below).
   auto fold_sum = [&]() __attribute__((always_inline)) {
     const float rs = lsum[0];
     bad = bad || !(rs <= FLT_MAX);
