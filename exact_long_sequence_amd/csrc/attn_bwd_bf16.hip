@@ -11,8 +11,9 @@
 //          (padding rows of each head get D = 0, lse = +inf);
 //   dk_dv: one workgroup per (batch*head, 128 keys); K and V of those keys stay
 //          in registers as MFMA operands while Q, dO and the row statistics of
-//          64-row query blocks stream through a three-stage LDS ring; the S and
-//          dP MFMAs of block i+1 run under the P / dS arithmetic of block i;
+//          64-row query blocks stream through a three- or four-stage LDS ring;
+//          the S and dP MFMAs of block i+1 run under the P / dS arithmetic of
+//          block i;
 //   dq:    one workgroup per (batch*head, 128 queries); Q and dO stay in
 //          registers while 64-key K/V tiles stream through an LDS ring (its own
 //          translation unit, attn_bwd_dq_bf16.hip, built with other options).
@@ -34,6 +35,8 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 #include "tile_ops.h"
 
@@ -42,6 +45,30 @@ namespace {
 
 constexpr int kStatPad = 64;  // workspace rows are padded per head to a multiple of this
 constexpr int kBwdBQ = 64;  // query rows per dK/dV pipeline step (32 measured slower)
+
+// LDS stages of the dK/dV ring, per head dimension: blocks i and i+1 are read
+// during step i and the DMA of block i+STAGES-1 is issued at its start, so a
+// block's load has STAGES-2 steps to land
+#ifndef ATTNIO_DKDV_STAGES_D64
+#define ATTNIO_DKDV_STAGES_D64 4
+#endif
+#ifndef ATTNIO_DKDV_STAGES_D128
+#define ATTNIO_DKDV_STAGES_D128 3
+#endif
+// 1: the causal compare runs only on the query blocks that meet the key
+// block's diagonal and the loop over the later blocks is built without it.
+// At d = 128 the second copy of the step pushes the kernel (512 registers)
+// into spills inside the loop, whose reloads wait for the DMAs in flight.
+#ifndef ATTNIO_DKDV_DIAG_MASK_D64
+#define ATTNIO_DKDV_DIAG_MASK_D64 1
+#endif
+#ifndef ATTNIO_DKDV_DIAG_MASK_D128
+#define ATTNIO_DKDV_DIAG_MASK_D128 0
+#endif
+constexpr int dkdv_stages(int d) { return d == 64 ? ATTNIO_DKDV_STAGES_D64 : ATTNIO_DKDV_STAGES_D128; }
+constexpr bool dkdv_diag_mask(int d) {
+  return d == 64 ? ATTNIO_DKDV_DIAG_MASK_D64 != 0 : ATTNIO_DKDV_DIAG_MASK_D128 != 0;
+}
 
 // ----------------------------------------------------------------------------
 // delta: D_i = dO_i . O_i (fp32) and lse_i * log2(e), per row.
@@ -78,7 +105,7 @@ void attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restric
 }
 
 // ----------------------------------------------------------------------------
-// dk_dv: 4 waves x 32 keys; 64-row query blocks through a three-stage LDS ring.
+// dk_dv: 4 waves x 32 keys; 64-row query blocks through a 3- or 4-stage LDS ring.
 //
 // One wave per SIMD, software-pipelined across query blocks: while the MFMAs of
 // S and dP for block i+1 run, the same wave computes P and dS of block i on the
@@ -92,7 +119,8 @@ struct KvCfg {
   static constexpr int RB = 2 * D;
   static constexpr int QT = BQ * RB;            // one Q or dO block
   static constexpr int STAGE = 2 * QT + 1024;   // Q, dO, row statistics (one 64-lane load)
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = dkdv_stages(D);
+  static_assert(STAGES == 3 || STAGES == 4, "dK/dV ring depth");
   static constexpr int LDS = STAGES * STAGE;
 };
 
@@ -195,6 +223,8 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       else
         dp[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ks], ks == 0 ? zero : dp[blk], 0, 0, 0);
     };
+    constexpr int AHEAD = C::STAGES - 1;    // DMA distance in blocks
+    constexpr int NLD = 2 * (BQ * 2 * D / 16 / C::THREADS);  // DMAs per block and wave (+1 on wave 0)
     constexpr int NQK = 2 * NB * (D / 16);  // MFMAs of S and dP per block
     constexpr int NEL = 16 * NB;            // scores per lane per block
     constexpr int R = 4;               // LDS read-ahead (MFMA slots)
@@ -225,7 +255,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // exponent is selected, not the result, so no branch forms around exp2.
     auto pds_elem = [&](const f32x16 (&s)[NB], const f32x16 (&dp)[NB], const float LDS_AS* st_f,
                         int tq, int m, f32x4& l4, f32x4& d4, bf16x8 (&pp)[BQ / 16],
-                        bf16x8 (&pds)[BQ / 16]) __attribute__((always_inline)) {
+                        bf16x8 (&pds)[BQ / 16], auto mask_tag) __attribute__((always_inline)) {
       const int blk = m / 16, a4 = (m % 16) / 4, e = m % 4, r = a4 * 4 + e;
       const int ql = blk * 32 + a4 * 8 + half * 4;  // first of four consecutive rows
       if (e == 0) {
@@ -233,7 +263,7 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         d4 = *(const f32x4 LDS_AS*)(st_f + BQ + ql);
       }
       float arg = __builtin_fmaf(s[blk][r], c, -l4[e]);
-      if (CAUSAL) arg = (tq <= blk * 32 + a4 * 8 + e) ? arg : -INFINITY;
+      if (decltype(mask_tag)::value) arg = (tq <= blk * 32 + a4 * 8 + e) ? arg : -INFINITY;
       const float p = __builtin_amdgcn_exp2f(arg);
       const float ds = p * (dp[blk][r] - d4[e]);  // p = 0 exactly where masked
       const int st = blk * 2 + a4 / 2, t8 = (a4 % 2) * 4 + e;
@@ -268,9 +298,9 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
     // one step: S / dP of block i+1 (if any) computed under P / dS of block i,
     // then dV / dK of block i
-    auto step = [&](int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB], f32x16 (&dpn)[NB])
-        __attribute__((always_inline)) {
-      if (i + 2 < nqb) issue(i + 2);
+    auto step = [&](int i, f32x16 (&s)[NB], f32x16 (&dp)[NB], f32x16 (&sn)[NB], f32x16 (&dpn)[NB],
+                    auto mask_tag) __attribute__((always_inline)) {
+      if (i + AHEAD < nqb) issue(i + AHEAD);
       const char LDS_AS* cur = smem + stage_of(i);
       const float LDS_AS* st_f = (const float LDS_AS*)(cur + 2 * QT);
       const int tq = key - (qb0 + i) * BQ - half * 4;  // below 0 on every block past the diagonal
@@ -288,29 +318,52 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
           // NEL scores over the NQK slots
 #pragma unroll
           for (int e = m * NEL / NQK; e < (m + 1) * NEL / NQK; ++e)
-            pds_elem(s, dp, st_f, tq, e, l4, d4, pp, pds);
+            pds_elem(s, dp, st_f, tq, e, l4, d4, pp, pds, mask_tag);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < NEL; ++e) pds_elem(s, dp, st_f, tq, e, l4, d4, pp, pds);
+        for (int e = 0; e < NEL; ++e) pds_elem(s, dp, st_f, tq, e, l4, d4, pp, pds, mask_tag);
       }
       pv_stream(i, pp, pds);
-      if (i + 2 < nqb) wait_dma_n<0>();
+      // block i+2 must be in LDS before step i+1; a later block may stay in flight
+      if (i + 2 < nqb) {
+        if (AHEAD > 2 && i + AHEAD < nqb) {
+          if (wave == 0) wait_dma_n<NLD + 1>();
+          else wait_dma_n<NLD>();
+        } else {
+          wait_dma_n<0>();
+        }
+      }
       __syncthreads();
     };
     issue(0);
-    if (nqb > 1) issue(1);
+#pragma unroll
+    for (int j = 1; j < AHEAD; ++j)
+      if (j < nqb) issue(j);
     wait_dma_n<0>();
     __syncthreads();
     f32x16 sA[NB], dpA[NB], sB[NB], dpB[NB];
     qk_only(0, sA, dpA);
+    // causal: the query blocks 0 .. NDIAG-1 of the loop meet the key block's
+    // diagonal; every later block lies wholly below it (all its scores visible)
+    using masked_t = std::integral_constant<bool, CAUSAL>;
+    using open_t = std::integral_constant<bool, CAUSAL && !dkdv_diag_mask(D)>;
+    constexpr int NDIAG = (CAUSAL && dkdv_diag_mask(D)) ? BKV / BQ : 0;
+    static_assert(NDIAG % 2 == 0, "diagonal blocks come in loop pairs");
     int i = 0;
-    for (; i + 1 < nqb; i += 2) {
-      step(i, sA, dpA, sB, dpB);
-      step(i + 1, sB, dpB, sA, dpA);
+    for (; i < NDIAG && i + 1 < nqb; i += 2) {
+      step(i, sA, dpA, sB, dpB, masked_t{});
+      step(i + 1, sB, dpB, sA, dpA, masked_t{});
     }
-    if (i < nqb) step(i, sA, dpA, sB, dpB);
+    for (; i + 1 < nqb; i += 2) {
+      step(i, sA, dpA, sB, dpB, open_t{});
+      step(i + 1, sB, dpB, sA, dpA, open_t{});
+    }
+    if (i < nqb) {
+      if (i < NDIAG) step(i, sA, dpA, sB, dpB, masked_t{});
+      else step(i, sA, dpA, sB, dpB, open_t{});
+    }
   }
 
   // lane (h, c) holds rows db*32 + (r/4)*8 + 4h + r%4 (head dimension) of its
