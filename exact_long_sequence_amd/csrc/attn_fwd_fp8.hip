@@ -10,11 +10,13 @@
 //     (x = fp8 * s); S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 with
 //     unit block scales, and the descales fold into the softmax constant;
 //   * the probabilities are rounded to E4M3 for O^T += V^T P^T on the same
-//     instruction.  The exponent shift is held at (running row maximum - 8),
-//     so every probability lies in (0, 256] (E4M3's largest finite value is
-//     448) and the row's largest entries sit at the top of the format, where
-//     its relative step is 2^-3; the shift moves, and the accumulator is
-//     rescaled, only when a tile raises the running maximum;
+//     instruction.  The exponent shift is (reference maximum - 8), where the
+//     reference follows the running row maximum lazily: it moves to a tile's
+//     maximum, and the accumulator is rescaled, only when that maximum exceeds
+//     it by more than 0.75 (base 2).  Every probability thus lies in
+//     (0, 2^8.75], below E4M3's largest finite value 448, and the row's
+//     largest entries sit at the top of the format, where its relative step
+//     is 2^-3;
 //   * the row sum l is the sum of the same E4M3 probabilities that multiply
 //     V, formed on the matrix core (an all-ones operand times P), so O =
 //     O^T * v_s / l is an exact convex combination of V's rows up to the
@@ -42,7 +44,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kFp8Shift = 8;  // log2 of the largest probability (256)
+constexpr int kFp8Shift = 8;  // log2 of the probability at the shift's reference maximum (256)
+// How far (base 2) a tile's maximum may rise above the reference before the
+// shift moves: probabilities then stay below 2^(8 + slack) = 430.5, under
+// E4M3's largest finite value 448, and the accumulator is rescaled only when a
+// row's maximum has grown by more than the slack since the last move.
+#ifndef ATTNIO_FP8_SLACK
+#define ATTNIO_FP8_SLACK 0.75f
+#endif
+constexpr float kFp8Slack = ATTNIO_FP8_SLACK;
+static_assert(kFp8Slack >= 0.f && kFp8Slack < 0.8f, "2^(8 + slack) must stay below 448");
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // format 0 (E4M3) for both operands, block scales 127 (= 2^0)
@@ -229,11 +240,14 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
         ext = fminf(ext, __shfl_xor(ext, 32));
       }
       const float tmax = ext * c;  // -inf when every score of the row is masked
-      // the shift follows the running maximum: rescale only when it rises
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run) != 0) {
-        const float m_new = fmaxf(m_run, tmax);
+      // the shift's reference moves to the tile maximum (and the accumulator is
+      // rescaled) only when that maximum exceeds the reference by more than the
+      // slack; -inf + slack = -inf, so a row's first visible tile always moves it
+      const bool mv = tmax > m_run + kFp8Slack;
+      if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+        const float m_new = mv ? tmax : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        if (m_new != m_run) {
+        if (mv) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -244,7 +258,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
         }
       }
       const float sh = m_run == -INFINITY ? 0.f : m_run - (float)kFp8Shift;
-      // P = 2^(s - sh) in (0, 256]; packed as E4M3 B operands: operand ps, byte
+      // P = 2^(s - sh) in (0, 2^(8 + slack)]; packed as E4M3 B operands: operand ps, byte
       // t = 16 b + r holds block 2 ps + b, register r
       i32x8 pb[BN / 64];
 #pragma unroll
