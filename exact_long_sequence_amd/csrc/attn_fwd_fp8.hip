@@ -43,6 +43,7 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFp8Shift = 8;  // log2 of the probability at the shift's reference maximum (256)
 // How far (base 2) a tile's maximum may rise above the reference before the
@@ -54,6 +55,15 @@ constexpr int kFp8Shift = 8;  // log2 of the probability at the shift's referenc
 #endif
 constexpr float kFp8Slack = ATTNIO_FP8_SLACK;
 static_assert(kFp8Slack >= 0.f && kFp8Slack < 0.8f, "2^(8 + slack) must stay below 448");
+
+// The value of lane l and of lane l ^ 32, in some order, by one
+// v_permlane32_swap with x as both operands (lanes 0-31 receive their
+// partner's value in the second element, lanes 32-63 in the first).  Every
+// lane of the wave must be active.
+__device__ __forceinline__ u32x2 pair_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (u32x2){r[0], r[1]};
+}
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // format 0 (E4M3) for both operands, block scales 127 (= 2^0)
@@ -231,13 +241,15 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) ext = fmaxf(ext, s[kb][r]);
-        ext = fmaxf(ext, __shfl_xor(ext, 32));
+        const u32x2 pr = pair_halves(ext);
+        ext = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       } else {
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) ext = fminf(ext, s[kb][r]);
-        ext = fminf(ext, __shfl_xor(ext, 32));
+        const u32x2 pr = pair_halves(ext);
+        ext = fminf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       }
       const float tmax = ext * c;  // -inf when every score of the row is masked
       // the shift's reference moves to the tile maximum (and the accumulator is
@@ -269,7 +281,10 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
           float p[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r0 + e], c, -sh));
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          // the low half is written first; the old value passed for the high
+          // half is p[0]'s own register (dead after this instruction, so no
+          // zeroing move), and the second conversion overwrites that half
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_bit_cast(int, p[0]), false);
           word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
           pb[ps][w] = word;
         }
