@@ -78,9 +78,10 @@ __global__ __launch_bounds__(256)
 void attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restrict__ dO,
                            const float* __restrict__ lse, float* __restrict__ ws_d,
                            float* __restrict__ ws_l, int N, int NP, long long rows_p) {
-  // one row of the padded [B*H][NP] statistics per LPR lanes; padding rows
-  // (i >= N) get D = 0 and lse = +inf, so a block that reads them computes
-  // P = 2^(s c - inf) = 0 and dS = 0 without a select
+  // one row of the padded statistics per LPR lanes; per head the NP values of
+  // D are followed by the NP values of lse*log2(e) ([B*H][2][NP]; ws_l =
+  // ws_d + NP).  Padding rows (i >= N) get D = 0 and lse = +inf, so a block
+  // that reads them computes P = 2^(s c - inf) = 0 and dS = 0 without a select
   constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long rp = gid / LPR;
@@ -99,8 +100,9 @@ void attn_bwd_delta_kernel(const __bf16* __restrict__ O, const __bf16* __restric
 #pragma unroll
   for (int off = LPR / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off, LPR);
   if (rp < rows_p && part == 0) {
-    ws_d[rp] = real ? acc : 0.f;
-    ws_l[rp] = real ? lse[row] * kLog2e : INFINITY;
+    const long long at = bh * 2 * NP + i;
+    ws_d[at] = real ? acc : 0.f;
+    ws_l[at] = real ? lse[row] * kLog2e : INFINITY;
   }
 }
 
@@ -128,7 +130,7 @@ template <int D, bool CAUSAL, int BQ_>
 __global__ __launch_bounds__(256, 1)
 void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                          const float* __restrict__ ws_d, long long l_off,
+                          const float* __restrict__ ws_d,
                           __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                           const int32_t* __restrict__ kv_len, int H, int N, int NP, float c,
                           float scale, int n_kblocks) {
@@ -199,11 +201,12 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       dma_rows<D, BQ, C::THREADS>(dOs, q0, N - 1, st + QT, wave, lane);
       if (wave == 0) {
         // lanes 0 .. BQ/4-1: lse*log2e of the BQ rows, the next BQ/4: D, the
-        // rest repeat them (the two workspace arrays are l_off floats apart)
+        // rest repeat them.  The scalar base is this head's statistics (64-bit
+        // address); the lane offset stays below 2 * NP * 4 bytes
         constexpr int NL = BQ / 4;
         const int sub = lane % (2 * NL);
-        const uint32_t off = (uint32_t)(((sub < NL ? l_off : 0LL) + (long long)bh * NP + q0 + 4 * (sub % NL)) * 4);
-        dma16(ws_d, off, __builtin_amdgcn_readfirstlane(st + 2 * QT));
+        const uint32_t off = ((sub < NL ? (uint32_t)NP : 0u) + (uint32_t)(q0 + 4 * (sub % NL))) * 4u;
+        dma16(ws_d + (size_t)bh * 2 * NP, off, __builtin_amdgcn_readfirstlane(st + 2 * QT));
       }
     };
 
@@ -392,8 +395,9 @@ void attn_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int NP = (a.N + kStatPad - 1) / kStatPad * kStatPad;
+  // per head: NP values of D, then NP values of lse*log2(e)
   float* ws_d = a.ws;
-  float* ws_l = a.ws + (size_t)a.B * a.H * NP;
+  float* ws_l = a.ws + NP;
   const long long rows_p = (long long)a.B * a.H * NP;
   const long long dgrid = (rows_p * (D / 8) + 255) / 256;
   const int n_kblocks = (a.N + 127) / 128;
@@ -409,7 +413,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   constexpr int kv_lds = KvCfg<D, kBwdBQ>::LDS;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, kBwdBQ>), dim3((unsigned)g_kv), dim3(256), kv_lds,
                      stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                     (const __bf16*)a.dout, ws_d, (long long)(ws_l - ws_d), (__bf16*)a.dk,
+                     (const __bf16*)a.dout, ws_d, (__bf16*)a.dk,
                      (__bf16*)a.dv, a.kv_len, a.H, a.N, NP, c, a.scale, n_kblocks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

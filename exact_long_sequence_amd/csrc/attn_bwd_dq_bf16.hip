@@ -78,8 +78,8 @@ void attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       qf[ks] = *(const bf16x8*)(Q + slice + (size_t)qr * D + ks * 16 + half * 8);
       dof[ks] = *(const bf16x8*)(dO + slice + (size_t)qr * D + ks * 16 + half * 8);
     }
-    lse2 = ws_l[(size_t)bh * NP + qr];
-    dlt = ws_d[(size_t)bh * NP + qr];
+    lse2 = ws_l[(size_t)bh * 2 * NP + qr];
+    dlt = ws_d[(size_t)bh * 2 * NP + qr];
   }
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(dof[ks]));
@@ -233,8 +233,8 @@ void attn_bwd_dq_pp_kernel(const __bf16* __restrict__ Q, const __bf16* __restric
       qf[ks] = *(const bf16x8*)(Q + slice + (size_t)qr * D + ks * 16 + half * 8);
       dof[ks] = *(const bf16x8*)(dO + slice + (size_t)qr * D + ks * 16 + half * 8);
     }
-    lse2 = ws_l[(size_t)bh * NP + qr];
-    dlt = ws_d[(size_t)bh * NP + qr];
+    lse2 = ws_l[(size_t)bh * 2 * NP + qr];
+    dlt = ws_d[(size_t)bh * 2 * NP + qr];
   }
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(dof[ks]));

@@ -39,10 +39,10 @@
 // running output and row sum).  The per-tile row maximum is not needed on the
 // common path.  A VALU row sum is tested before the tile's P x V (the tile is
 // recomputed after moving the shift).  A matrix-core row sum is known one
-// MFMA phase after its P, so the test comes after the tile's P x V; if an
-// exp2 overflowed there (a score more than 2^7 above the shift in the base-2
-// domain), the workgroup computes its rows again with the shift checked
-// before every tile.
+// MFMA phase after its P, so the test comes after the tile's P x V; if that
+// sum exceeds 2^64 (a probability that large times |V| could have overflowed
+// the fp32 accumulator) or is not finite (an exp2 overflowed), the workgroup
+// computes its rows again with the shift checked before every tile.
 //
 // Two loop forms share the per-tile building blocks (selected per head size
 // at the bottom of this file):
@@ -82,6 +82,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTauLog2 = 8.0f;        // shift moves when a row maximum exceeds it by 2^8
 constexpr float kLazySumMax = 65536.f;  // a tile row sum above this moves the shift
+// A matrix-core row sum is tested after the tile's P x V is already in the
+// fp32 accumulator.  Every partial sum of that product is bounded by
+// (tile row sum) * max|V|, so a tile whose row sum stays at or below 2^64
+// cannot have overflowed it while max|V| < 2^63; a larger sum (finite or not)
+// sends the workgroup to the safe pass.  Testing only for a non-finite sum
+// would miss probabilities up to 2^128, finite in bf16 and fp32, whose
+// products with |V| > 1 overflow.
+constexpr float kSafeSumMax = 0x1p64f;
 
 // Where the row sums of P are formed: on the matrix core (next to the P x V
 // MFMAs, one tile late) or on the VALU (two-element dot products, in the
@@ -557,14 +565,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // rescale of acc and l).  Any shift gives the same softmax (it cancels
   // between numerator and denominator), so the result is exact up to
   // rounding.  The test comes one tile late, after the tile's P x V: a sum
-  // that is not finite means some exp2 overflowed, and the workgroup then
+  // above kSafeSumMax (or not finite: some exp2 overflowed) means the
+  // accumulator may already hold an overflowed product, and the workgroup then
   // recomputes its rows with the shift checked before every tile (the safe
   // pass below).
   auto fold_sum = [&]() __attribute__((always_inline)) {
     const float rs = lsum[0];
-    bad = bad || !(rs <= FLT_MAX);
+    bad = bad || !(rs <= kSafeSumMax);
     l_run += rs;
-    if (rs > kLazySumMax && rs <= FLT_MAX) {
+    if (rs > kLazySumMax && rs <= kSafeSumMax) {
       const float mv = floorf(__builtin_amdgcn_logf(rs));
       const float alpha = __builtin_amdgcn_exp2f(-mv);
       m_run += mv;

@@ -43,6 +43,12 @@ bool current_device_is_gfx950() {
   return g_dev_ok[dev] == 1;
 }
 
+// hipGetLastError() returns and clears the calling thread's last HIP error.
+// Called once the arguments are accepted and before anything is enqueued, so
+// that the status read after the launches names those launches only, not an
+// unrelated earlier HIP call of the caller.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
 bool overlaps(const void* a, const void* b, size_t bytes) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + bytes && y < x + bytes;
@@ -82,6 +88,7 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
       return ATTN_E_ALIAS;
   }
   if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  clear_stale_hip_error();
   attnio::FwdArgs a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0, want_lse ? lse : nullptr};
   if (log_enabled()) {
     attnio::Tiling t{};
@@ -162,6 +169,7 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
       if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return ATTN_E_ALIAS;
   }
   if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  clear_stale_hip_error();
   attnio::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, kv_len, B, H, N, d, scale,
                     causal ? 1 : 0};
   const hipError_t e = attnio::launch_bwd_bf16(a, (hipStream_t)stream);
@@ -190,6 +198,7 @@ int attn_fwd_unfused(const void* Q, const void* K, const void* V, void* O, void*
   for (int j = 0; j < 4; ++j)
     if (ranges_overlap(workspace, workspace_bytes, ins[j], tb)) return ATTN_E_ALIAS;
   if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  clear_stale_hip_error();
   attnio::UnfusedArgs a{Q, K, V, O, workspace, workspace_bytes, kv_len, B, H, N, d, scale,
                         causal ? 1 : 0};
   const hipError_t e = attnio::launch_unfused_bf16(a, (hipStream_t)stream);
@@ -210,11 +219,16 @@ int attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, int B, in
   if (!std::isfinite(scale)) return ATTN_E_ARG;
   for (float s : {q_descale, k_descale, v_descale})
     if (!std::isfinite(s) || !(s > 0.f)) return ATTN_E_ARG;
+  // the kernel folds scale, both descales and log2(e) into one fp32 exponent
+  // multiplier (same product, same order as its launcher); finite factors
+  // whose product overflows would turn every score into +-inf and O into NaN
+  if (!std::isfinite(scale * q_descale * k_descale * 1.4426950408889634f)) return ATTN_E_ARG;
   const size_t in_b = (size_t)B * H * N * d, out_b = 2 * in_b;
   if (ranges_overlap(O, out_b, Q, in_b) || ranges_overlap(O, out_b, K, in_b) ||
       ranges_overlap(O, out_b, V, in_b))
     return ATTN_E_ALIAS;
   if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  clear_stale_hip_error();
   attnio::Fp8Args a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0,
                     q_descale, k_descale, v_descale};
   const hipError_t e = attnio::launch_fwd_fp8(a, (hipStream_t)stream);
@@ -239,6 +253,7 @@ int run_rows(const void* X, const void* gamma, const void* beta, void* Y, int R,
   if ((gamma && ranges_overlap(gamma, vb, Y, xb)) || (beta && ranges_overlap(beta, vb, Y, xb)))
     return ATTN_E_ALIAS;
   if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  clear_stale_hip_error();
   attnio::RowArgs a{X, Y, gamma, beta, R, N, op, param};
   const hipError_t e = attnio::launch_stream_rows(a, (hipStream_t)stream);
   if (e != hipSuccess) {

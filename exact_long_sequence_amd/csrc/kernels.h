@@ -97,7 +97,9 @@ hipError_t launch_unfused_bf16(const UnfusedArgs& a, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int H, int N);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 // dQ stage of the backward (ws_d / ws_l: the delta kernel's padded statistics,
-// NP rows per head; c = scale * log2(e)).
+// per head NP values of D then NP of lse*log2(e), so head bh's row i is at
+// ws_d[bh*2*NP + i] and ws_l[bh*2*NP + i] with ws_l = ws_d + NP;
+// c = scale * log2(e)).
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* ws_d, const float* ws_l, int NP,
                               float c, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

@@ -99,7 +99,9 @@ __device__ __forceinline__ void dma_rows(const __bf16* gsrc, int r0, int last_ok
     const int lch = pch ^ swz<D>(row);
     int grow = r0 + row;
     grow = grow < last_ok ? grow : last_ok;
-    const uint32_t o = (uint32_t)(grow * RB + lch * 16);
+    // unsigned: a head holds fewer than 2^31 elements, so the byte offset of
+    // its last row fits 32 bits unsigned (not signed, at N > 2^23, d = 128)
+    const uint32_t o = (uint32_t)grow * (uint32_t)RB + (uint32_t)(lch * 16);
     const uint32_t l = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((i * THREADS + wave * 64) * 16));
     dma16(gsrc, o, l);
   }

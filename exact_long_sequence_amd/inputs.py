@@ -104,20 +104,36 @@ def oracle_view(t: torch.Tensor) -> np.ndarray:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def sample_rows(B: int, H: int, N: int, n_sample: int, seed: int, boundary_bm: int = 128,
+# Query-tile heights of the kernels' tilings (rows per workgroup and, for the
+# smaller ones, per wave group): rows on both sides of every multiple of these
+# up to 1024 are forced into each sample.
+TILE_EDGES = (32, 64, 128, 256, 512)
+
+
+def sample_rows(B: int, H: int, N: int, n_sample: int, seed: int, boundary_bms=TILE_EDGES,
                 kv_len=None) -> np.ndarray:
     """Seeded sample of flat (b*H + h)*N + i query-row indices, plus boundary rows.
 
-    Boundary rows: i in {0, 1, BM-1, BM, N-2, N-1} of the first and last (b, h)
-    slices, and, with key padding, the rows i = L-1 and L of the first head of
-    the batches with the smallest and largest length L."""
+    Boundary rows, in the first and last (b, h) slices: i in {0, 1, N-2, N-1}
+    and i in {k*BM - 1, k*BM} for every BM in boundary_bms and k*BM <= 1024
+    (the edges of the query tiles), plus the last tile edges below N.  With key
+    padding, also the rows i = L-1 and L of the first head of the batches with
+    the smallest and largest length L."""
     total = B * H * N
     rng = np.random.default_rng(int(seed) + 1)
     n = min(n_sample, total)
     picked = rng.choice(total, n, replace=False)
+    if isinstance(boundary_bms, int):
+        boundary_bms = (boundary_bms,)
+    edge_rows = {0, 1, N - 2, N - 1}
+    for bm in boundary_bms:
+        for e in range(bm, min(N, 1024) + 1, bm):
+            edge_rows.update((e - 1, e))
+        last = (N - 1) // bm * bm
+        edge_rows.update((last - 1, last))
     extra = []
     for (b, h) in {(0, 0), (B - 1, H - 1)}:
-        for i in (0, 1, boundary_bm - 1, boundary_bm, N - 2, N - 1):
+        for i in sorted(edge_rows):
             if 0 <= i < N:
                 extra.append((b * H + h) * N + i)
     if kv_len is not None:

@@ -122,9 +122,12 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
  * inputs are x = fp8(x) * x_descale with one finite, positive fp32 descale per
  * tensor.  O is bf16 [B, H, N, d] (2 bytes per element; must not overlap the
  * inputs).  Q K^T and P V run on gfx950's fp8 matrix cores with fp32
- * accumulation; the probabilities are rounded to E4M3 (in (0, 256] relative to
- * the running row maximum) for the P V product, the row sum uses the unrounded
- * fp32 probabilities, and O is rounded to bf16 once.  Other conventions
+ * accumulation; the probabilities are rounded to E4M3 for the P V product, in
+ * (0, 2^8.75 = 430.5] relative to an exponent shift that trails the running
+ * row maximum by at most 0.75 (base 2); the row sum is the sum of those same
+ * rounded probabilities (formed on the matrix core), and O is rounded to bf16
+ * once.  Returns ATTN_E_ARG if a descale is not finite and positive, or if
+ * scale * q_descale * k_descale * log2(e) overflows fp32.  Other conventions
  * (d, N, scale, causal, kv_len, stream, errors) as for attn_fwd. */
 int attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
                  float scale, float q_descale, float k_descale, float v_descale, int causal,

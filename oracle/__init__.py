@@ -5,7 +5,6 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP path.
 """
 from .attention import (  # noqa: F401
-    allowed_key_count,
     allowed_mask,
     attention_fp64,
     attention_full_fp64,

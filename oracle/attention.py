@@ -48,7 +48,6 @@ __all__ = [
     "attention_fp64",
     "attention_rows_fp64",
     "attention_full_fp64",
-    "allowed_key_count",
     "attention_lse_fp64",
     "attention_bwd_fp64",
     "attention_bwd_rows_fp64",
@@ -223,14 +222,6 @@ def attention_full_fp64(q, k, v, scale: float, causal: bool = False, kv_len=None
                                           causal, int(Ls[b]), want_p=True)
             O[b, h], P[b, h], lse[b, h] = o, p, l
     return O, P, lse
-
-
-def allowed_key_count(rows_i: np.ndarray, L: int, N: int, causal: bool) -> np.ndarray:
-    """Number of keys each query row i may attend to (the work of that row)."""
-    i = np.asarray(rows_i, dtype=np.int64)
-    if causal:
-        return np.minimum(i + 1, L)
-    return np.full(i.shape, min(L, N), dtype=np.int64)
 
 
 def attention_lse_fp64(q, k, v, scale: float, causal: bool = False, kv_len=None,

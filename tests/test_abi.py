@@ -143,6 +143,9 @@ def test_fp8_entry_argument_errors(lib):
     assert call(q=0x100008) == -4
     assert call(scale=float("nan")) == -8
     assert call(qs=0.0) == -8 and call(ks=-1.0) == -8 and call(vs=float("inf")) == -8
+    # finite descales whose folded exponent multiplier overflows fp32
+    assert call(qs=2.0 ** 100, ks=2.0 ** 100) == -8
+    assert call(scale=-2.0 ** 120, qs=2.0 ** 10) == -8
     assert call(o=0x300000 - 1024) == -7       # 2 KiB of bf16 output reaches into V's 1 KiB
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():

@@ -11,9 +11,11 @@ the format's normal range, and the row sum is the sum of those same rounded
 values, so O = sum_j P_j (1 + d_j) V_j / (1 + db) with db = sum_j P_j d_j:
 O - O_ref = (sum_j P_j d_j V_j - db O_ref) / (1 + db), at most
 2^-4 (M + |O_ref|) / (1 - 2^-4) = (M + |O_ref|) / 15; the output's bf16
-rounding adds 2^-9 |O|.  Probabilities in E4M3's subnormal range (below 2^-14
-of the row maximum, since the kernel keeps the maximum at 256) round with an
-absolute error of at most 2^-18 of the maximum each; with the fp32
+rounding adds 2^-9 |O|.  Probabilities in E4M3's subnormal range (below 2^-6,
+that is 2^-14 to 2^-14.75 of the row's largest probability, which the kernel
+keeps in [2^8, 2^8.75 = 430.5] by letting its exponent shift trail the running
+maximum by up to 0.75) round with an absolute error of at most 2^-10, at most
+2^-18 of the largest probability each; with the fp32
 accumulation they stay far inside the 2e-3 term (a CPU model of exactly these
 roundings, per-tile shifts included, exceeds the first two terms by at most
 5e-6 on the shapes below, reaches at most 0.59 of the bound, and its mean

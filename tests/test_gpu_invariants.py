@@ -3,8 +3,9 @@
 Closed forms and invariants of the definition (constant values, zero scale,
 masked keys contributing nothing, fully masked rows), run-to-run determinism,
 stream ordering, a negative scale, an input that forces the running maximum to
-grow on every key tile, an input whose probabilities overflow the first
-tile's exponent shift, and the largest supported tensor size.
+grow on every key tile, inputs whose probabilities overflow the first tile's
+exponent shift (exp2 itself, or only their products with V), and the largest
+supported tensor size.
 """
 
 import math
@@ -55,14 +56,23 @@ def test_poisoned_padding_keys_do_not_leak(dtype, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_bitwise_determinism(d):
-    q, k, v, kv = make_inputs(2, 4, 3000, d, "bf16", seed=32, padded=True)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bitwise_determinism(d, causal):
+    """Run-to-run bitwise equality over 24 calls, alternating between two
+    output buffers (a stale buffer cannot pass for a fresh one) with the
+    default-launch-order work of a different call in between."""
+    q, k, v, kv = make_inputs(2, 8, 3000, d, "bf16", seed=32, padded=True)
     qd, kd, vd, kvd = q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV)
-    ref = attnio.attn_fwd(qd, kd, vd, causal=True, kv_len=kvd)
-    for _ in range(5):
-        o = attnio.attn_fwd(qd, kd, vd, causal=True, kv_len=kvd)
+    ref = attnio.attn_fwd(qd, kd, vd, causal=causal, kv_len=kvd)
+    outs = [torch.full_like(qd, float("nan")) for _ in range(2)]
+    other = torch.empty_like(qd)
+    for i in range(24):
+        o = outs[i % 2]
+        o.fill_(float("nan"))
+        attnio.attn_fwd(qd, kd, vd, causal=causal, kv_len=kvd, out=o)
+        attnio.attn_fwd(kd, qd, vd, causal=not causal, out=other)
         torch.cuda.synchronize()
-        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), f"call {i}"
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -160,6 +170,35 @@ def test_probability_overflow_recomputed(d, causal):
     out = run_gpu(q, k, v, causal, None, 1.0, "bf16")
     want = oracle_rows(q, k, v, causal, None, 1.0, "bf16")
     compare(gpu_rows(out), want, "bf16", f"overflow d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_finite_probability_overflow_recomputed(d, causal):
+    """One or two keys per head score 88 (x log2 e = 126.96 in the exponent)
+    above every other key on even rows, whose scores are all exactly 0.  The
+    exponent shift taken from the first key tile is then 0, the spike's
+    probability 2^126.96 is finite in bf16 and fp32, and so is the tile's row
+    sum, but its product with |V| = 4 overflows fp32.  The fast pass must send
+    the workgroup to the safe pass (d = 128: the row sum is tested after the
+    tile's P x V) or recompute the tile before its P x V (d = 64); O must be
+    finite and match the oracle on every row."""
+    N = 1000
+    _log(f"finite-P overflow d={d} causal={causal}")
+    g = torch.Generator().manual_seed(41)
+    q = torch.zeros(1, 2, N, d)
+    q[..., 0] = torch.where(torch.arange(N) % 2 == 0, 1.0, 0.05)
+    k = torch.zeros(1, 2, N, d)
+    spikes = {0: (130, 700), 1: (500,)}
+    v = torch.randn(1, 2, N, d, generator=g)
+    for h, js in spikes.items():
+        for j in js:
+            k[0, h, j, 0] = 88.0
+            v[0, h, j] = 4.0 * torch.sign(torch.randn(d, generator=g))
+    q, k, v = (t.to(torch.bfloat16).contiguous() for t in (q, k, v))
+    out = run_gpu(q, k, v, causal, None, 1.0, "bf16")
+    want = oracle_rows(q, k, v, causal, None, 1.0, "bf16")
+    compare(gpu_rows(out), want, "bf16", f"finite-P overflow d={d} causal={causal}")
 
 
 def test_non_default_stream_ordering():
