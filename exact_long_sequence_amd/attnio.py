@@ -20,7 +20,7 @@ _lib = None
 
 ATTN_OK = 0
 
-__all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
+__all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd", "attn_bwd_noalloc",
            "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
            "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_fwd_fp8", "attn_strerror", "attn_version", "attn_query_tiling",
            "attn_io_model", "library_path", "load_library"]
@@ -50,6 +50,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = i32
     lib.attn_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_bwd_noalloc.argtypes = [vp] * 9 + [i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.attn_bwd_noalloc.restype = i32
     lib.attn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fwd_unfused.argtypes = [vp] * 5 + [ctypes.c_size_t, i32, i32, i32, i32, f32, i32, vp, vp]
@@ -209,6 +211,44 @@ def attn_fwd_f32_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
 def attn_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
     """Device workspace bytes attn_bwd needs (0 for non-positive sizes)."""
     return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     dout: torch.Tensor, lse: torch.Tensor, *, causal: bool = False,
+                     kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                     dv: Optional[torch.Tensor] = None):
+    """attn_bwd without a workspace: the library's static device scratch holds
+    the row statistics (at most ATTN_NOALLOC_SCRATCH_BYTES).  Pass dq, dk, dv
+    to make the call itself allocate nothing.  Returns (dq, dk, dv)."""
+    lib = load_library()
+    _check(q, k, v, torch.bfloat16)
+    _check(o, dout, q, torch.bfloat16)
+    B, H, N, d = q.shape
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32
+            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor like q")
+        grads.append(t)
+    kv_len, kv_ptr = _kv_len_ptr(kv_len, B, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  dout.data_ptr(), lse.data_ptr(), grads[0].data_ptr(),
+                                  grads[1].data_ptr(), grads[2].data_ptr(), B, H, N, d, float(scale),
+                                  int(bool(causal)), kv_ptr, stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_bwd_noalloc: {attn_strerror(rc)} (code {rc})")
+    return tuple(grads)
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,

@@ -115,6 +115,89 @@ double pair_count(long long N, long long L, bool causal) {
   return (double)L * (double)(L + 1) / 2.0 + (double)(N - L) * (double)L;
 }
 
+// ---------------------------------------------------------------------------
+// Backward scratch without allocation.  attn_bwd_noalloc keeps the backward's
+// row statistics in this file-scope device array instead of a caller
+// workspace, for callers that cannot allocate.  Each device holds its own copy
+// at its own address; in host code `scratch` only names the symbol, so its
+// device address is looked up once per device (with that device current) and
+// only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of this device's scratch array, or nullptr (with the HIP error
+// in *err) if it could not be looked up.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    if (*err == hipSuccess) *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+// Argument checks and launch of the backward.  With check_ws the workspace is
+// the caller's (checked for alignment and overlap); otherwise it is this
+// device's scratch array.  checks_only: return after the host-side checks.
+int run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+            const float* LSE, void* dQ, void* dK, void* dV, void* workspace, bool check_ws, int B,
+            int H, int N, int d, float scale, int causal, const int32_t* kv_len, void* stream,
+            bool checks_only = false) {
+  if (!dO || !LSE || !dQ || !dK || !dV) return ATTN_E_NULL;
+  int rc = validate(Q, K, V, dQ, B, H, N, d, scale, 2);
+  if (rc != ATTN_OK) return rc;
+  if (!O) return ATTN_E_NULL;
+  const size_t tb = (size_t)B * H * N * d * 2;
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const size_t wb = attnio::bwd_workspace_bytes(B, H, N);
+  if ((((uintptr_t)O | (uintptr_t)dO | (uintptr_t)dK | (uintptr_t)dV |
+        (check_ws ? (uintptr_t)workspace : 0u)) & 15u) ||
+      ((uintptr_t)LSE & 3u))
+    return ATTN_E_ALIGN;
+  // outputs must not overlap any input, each other, or the workspace
+  const void* ins[6] = {Q, K, V, O, dO, LSE};
+  const size_t in_b[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dQ, dK, dV, workspace};
+  const size_t out_b[4] = {tb, tb, tb, wb};
+  const int n_out = check_ws ? 4 : 3;
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return ATTN_E_ALIAS;
+    for (int j = i + 1; j < n_out; ++j)
+      if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return ATTN_E_ALIAS;
+  }
+  if (checks_only) return ATTN_OK;
+  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
+  if (!check_ws) {
+    hipError_t se = hipSuccess;
+    workspace = scratch_on_current_device(&se);
+    if (workspace == nullptr) {
+      if (log_enabled()) fprintf(stderr, "[attnio] scratch lookup failed: %s\n", hipGetErrorString(se));
+      return ATTN_E_LAUNCH;
+    }
+  }
+  clear_stale_hip_error();
+  attnio::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, kv_len, B, H, N, d, scale,
+                    causal ? 1 : 0};
+  const hipError_t e = attnio::launch_bwd_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    if (log_enabled()) fprintf(stderr, "[attnio] backward launch failed: %s\n", hipGetErrorString(e));
+    return ATTN_E_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,37 +230,22 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N) {
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
              const float* LSE, void* dQ, void* dK, void* dV, void* workspace, int B, int H, int N,
              int d, float scale, int causal, const int32_t* kv_len, void* stream) {
-  if (!dO || !LSE || !dQ || !dK || !dV || !workspace) return ATTN_E_NULL;
-  int rc = validate(Q, K, V, dQ, B, H, N, d, scale, 2);
-  if (rc != ATTN_OK) return rc;
-  if (!O) return ATTN_E_NULL;
-  const size_t tb = (size_t)B * H * N * d * 2;
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const size_t wb = attnio::bwd_workspace_bytes(B, H, N);
-  if ((((uintptr_t)O | (uintptr_t)dO | (uintptr_t)dK | (uintptr_t)dV | (uintptr_t)workspace) & 15u) ||
-      ((uintptr_t)LSE & 3u))
-    return ATTN_E_ALIGN;
-  // outputs must not overlap any input, each other, or the workspace
-  const void* ins[6] = {Q, K, V, O, dO, LSE};
-  const size_t in_b[6] = {tb, tb, tb, tb, tb, lb};
-  void* outs[4] = {dQ, dK, dV, workspace};
-  const size_t out_b[4] = {tb, tb, tb, wb};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (ranges_overlap(outs[i], out_b[i], ins[j], in_b[j])) return ATTN_E_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (ranges_overlap(outs[i], out_b[i], outs[j], out_b[j])) return ATTN_E_ALIAS;
+  if (!workspace) return ATTN_E_NULL;
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, true, B, H, N, d, scale, causal, kv_len,
+                 stream);
+}
+
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                     float scale, int causal, const int32_t* kv_len, void* stream) {
+  if (B >= 1 && H >= 1 && N >= 1 && attnio::bwd_workspace_bytes(B, H, N) > kScratchBytes) {
+    // run the ordinary checks first so that a bad pointer still reports as such
+    const int rc = run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, nullptr, false, B, H, N, d, scale, causal,
+                           kv_len, stream, /*checks_only=*/true);
+    return rc != ATTN_OK ? rc : ATTN_E_SCRATCH;
   }
-  if (!current_device_is_gfx950()) return ATTN_E_DEVICE;
-  clear_stale_hip_error();
-  attnio::BwdArgs a{Q, K, V, O, dO, LSE, dQ, dK, dV, (float*)workspace, kv_len, B, H, N, d, scale,
-                    causal ? 1 : 0};
-  const hipError_t e = attnio::launch_bwd_bf16(a, (hipStream_t)stream);
-  if (e != hipSuccess) {
-    if (log_enabled()) fprintf(stderr, "[attnio] backward launch failed: %s\n", hipGetErrorString(e));
-    return ATTN_E_LAUNCH;
-  }
-  return ATTN_OK;
+  return run_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, nullptr, false, B, H, N, d, scale, causal, kv_len,
+                 stream);
 }
 
 size_t attn_fwd_unfused_workspace_bytes(int N) {
@@ -286,6 +354,9 @@ const char* attn_strerror(int code) {
     case ATTN_E_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case ATTN_E_ALIAS: return "O overlaps Q, K or V";
     case ATTN_E_ARG: return "argument out of range (scale must be finite)";
+    case ATTN_E_SCRATCH:
+      return "the backward's statistics need more than the allocation-free entry point's static "
+             "scratch (ATTN_NOALLOC_SCRATCH_BYTES); use attn_bwd with a workspace";
     default: return "unknown attnio status code";
   }
 }

@@ -56,7 +56,8 @@ enum {
   ATTN_E_LAUNCH = -5,    /* the kernel launch was rejected by the HIP runtime */
   ATTN_E_DEVICE = -6,    /* the current device is not a gfx950 GPU */
   ATTN_E_ALIAS = -7,     /* O overlaps Q, K or V */
-  ATTN_E_ARG = -8        /* another argument is out of range */
+  ATTN_E_ARG = -8,       /* another argument is out of range */
+  ATTN_E_SCRATCH = -9    /* attn_bwd_noalloc: the shape needs more than its static scratch */
 };
 
 /* bf16 attention forward: Q, K, V, O hold bfloat16 values.  Products run on
@@ -115,6 +116,26 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
 /* Bytes of device workspace attn_bwd needs for B x H heads of N rows (host
  * only; 0 for non-positive sizes). */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
+/* Size of the static device scratch of attn_bwd_noalloc (32 MiB per GPU). */
+#define ATTN_NOALLOC_SCRATCH_BYTES 33554432u
+
+/* attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels, results and errors as
+ * attn_bwd, whose workspace is replaced by a static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; the call itself allocates nothing (its first call on
+ * a device looks up that device's copy of the array, once).  Shapes whose
+ * attn_bwd_workspace_bytes(B, H, N) exceeds ATTN_NOALLOC_SCRATCH_BYTES return
+ * ATTN_E_SCRATCH (B*H*ceil(N/64)*64 must be at most 4194304 rows).  Every call
+ * on one GPU shares that GPU's array and nothing in it needs to start at zero;
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race on it, so such callers must order them. */
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, void* dQ, void* dK, void* dV,
+                     int B, int H, int N, int d, float scale, int causal,
+                     const int32_t* kv_len, void* stream);
 
 /* fp8 attention forward (quantisation effects, as the Neural Circuit Diagrams
  * abstract lists them among what its performance model covers).  Q, K, V are

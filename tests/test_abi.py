@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_strerror_and_version(lib):
     assert attnio.attn_version() >= 100
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = attnio.attn_strerror(code)
         assert s and "unknown" not in s
     assert "unknown" in attnio.attn_strerror(-99)
@@ -112,6 +112,32 @@ def test_bwd_entry_argument_errors(lib):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         assert call() == -6
+
+
+def test_bwd_noalloc_host_checks(lib):
+    """The allocation-free backward checks its arguments like attn_bwd and
+    refuses, on the host, shapes whose statistics exceed its static scratch."""
+    base = {"Q": 0x100000, "K": 0x200000, "V": 0x300000, "O": 0x400000, "dO": 0x500000,
+            "LSE": 0x600000, "dQ": 0x700000, "dK": 0x800000, "dV": 0x900000}
+
+    def call(B=1, H=1, N=16, d=64, **over):
+        p = dict(base, **over)
+        return lib.attn_bwd_noalloc(p["Q"], p["K"], p["V"], p["O"], p["dO"], p["LSE"], p["dQ"],
+                                    p["dK"], p["dV"], B, H, N, d, ctypes.c_float(0.125), 0, None, None)
+    for name in base:
+        assert call(**{name: None}) == -1, name
+    assert call(d=96) == -2 and call(N=0) == -3
+    assert call(dQ=base["Q"] + 1024) == -7
+    # 4194304 padded rows of 8 bytes fill the 32 MiB scratch exactly; 64 more do not
+    assert attnio.attn_bwd_workspace_bytes(1, 4096, 1024) == 32 * 1024 * 1024
+    G = 1 << 30
+    big = {k: (i + 1) * G for i, k in enumerate(base)}
+    assert call(B=1, H=4097, N=1024, **big) == -9
+    assert call(B=1, H=4097, N=1024, **dict(big, Q=None)) == -1   # pointer checks come first
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert call() == -6
+        assert call(B=1, H=4096, N=1024, **big) == -6               # fits: reaches the device check
 
 
 def test_unfused_entry_argument_errors(lib):
