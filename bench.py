@@ -17,6 +17,7 @@ a bounded row sample on the host cores (which also checks those rows).
   python bench.py --mode unfused [--workload NAME] [--heads-per-pass G]
   python bench.py --mode rows [--workload softmax_r32k_n32k|layernorm_r128k_n8k]
   python bench.py --mode fp8 [--workload NAME]   # the workload's shape with E4M3 inputs
+  python bench.py --mode tilings --all-workloads  # every compiled tiling vs the I/O model's pick
   python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
 
 In --mode bwd one step is one attn_bwd call (its three kernels) from the
@@ -452,6 +453,61 @@ def bench_fp8(w, args) -> int:
     return 0
 
 
+def bench_tilings(args) -> int:
+    """Every compiled bf16 forward tiling of the workload's head size, timed
+    interleaved on the same GPU (median of args.reps rounds of args.steps
+    launches each), next to the I/O model's choice and predicted cost.  One
+    JSON line per workload."""
+    import torch
+
+    from exact_long_sequence_amd import attnio
+    from exact_long_sequence_amd.inputs import WORKLOADS, workload_inputs
+    names = args.workload.split(",")
+    if args.all_workloads:
+        names = [n for n, w in WORKLOADS.items() if w.dtype == "bf16"]
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v, kv_len = workload_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        kvd = None if kv_len is None else kv_len.to(dev)
+        out = torch.empty_like(qd)
+        model = attnio.attn_io_model(w.B, w.H, w.N, w.d, 2, w.causal,
+                                     None if kv_len is None else kv_len.tolist())
+        ranking = attnio.attn_tiling_enumerate(w.d, w.causal)
+        rank_of = {e["compiled"]: r for r, e in enumerate(ranking) if e["compiled"] >= 0}
+        pick = next(e["compiled"] for e in ranking if e["compiled"] >= 0)
+        idx = [i for i in range(attnio.attn_tiling_count()) if attnio.attn_tiling_get(i)["d"] == w.d]
+        for i in idx:
+            for _ in range(args.warmup):
+                attnio.attn_fwd_tiled(qd, kd, vd, i, causal=w.causal, kv_len=kvd, scale=w.scale, out=out)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        times = {i: [] for i in idx}
+        for _ in range(args.reps):
+            for i in idx:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(args.steps):
+                    attnio.attn_fwd_tiled(qd, kd, vd, i, causal=w.causal, kv_len=kvd, scale=w.scale, out=out)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[i].append(e0.elapsed_time(e1) / args.steps)
+        rows = []
+        for i in idx:
+            ms = sorted(times[i])[len(times[i]) // 2]
+            ev = ranking[rank_of[i]]
+            rows.append({"tiling": i, **attnio.attn_tiling_get(i), "model_rank": rank_of[i],
+                         "model_cycles_per_pair": ev["cycles_per_pair"], "ms_median": ms,
+                         "ms_all": times[i], "tflops": model["flops"] / (ms * 1e-3) / 1e12})
+        best = min(rows, key=lambda r: r["ms_median"])["tiling"]
+        print(json.dumps({"mode": "tilings", "workload": name, "model_pick": pick, "measured_best": best,
+                          "steps": args.steps, "reps": args.reps, "results": rows}), flush=True)
+        del qd, kd, vd, out
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,7 +517,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
-    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused", "rows", "fp8"), default="fwd")
+    ap.add_argument("--mode", choices=("fwd", "bwd", "unfused", "rows", "fp8", "tilings"), default="fwd")
+    ap.add_argument("--reps", type=int, default=4, help="--mode tilings: interleaved rounds per tiling")
+    ap.add_argument("--all-workloads", action="store_true", help="--mode tilings: every bf16 workload")
+    ap.add_argument("--tiling", type=int, default=-1,
+                    help="--mode fwd: run this compiled tiling (attn_tiling_get index) instead of the model's")
     ap.add_argument("--heads-per-pass", type=int, default=8,
                     help="--mode unfused: heads whose N x N intermediates share the workspace")
     args = ap.parse_args()
@@ -483,6 +543,8 @@ def main() -> int:
 
     if args.mode == "rows":
         return bench_rows(args)
+    if args.mode == "tilings":
+        return bench_tilings(args)
     w = WORKLOADS[args.workload]
     if args.mode == "bwd":
         return bench_bwd(w, args)
@@ -496,9 +558,20 @@ def main() -> int:
     kvd = None if kv_len is None else kv_len.to(dev)
     out = torch.empty_like(qd)
     fn = attnio.attn_fwd if w.dtype == "bf16" else attnio.attn_fwd_f32
+    if args.tiling >= 0:
+        if w.dtype != "bf16":
+            print("--tiling selects a bf16 tiling", file=sys.stderr)
+            return 2
+        fn = lambda q_, k_, v_, **kw: attnio.attn_fwd_tiled(q_, k_, v_, args.tiling, **kw)  # noqa: E731
     model = attnio.attn_io_model(w.B, w.H, w.N, w.d, 2 if w.dtype == "bf16" else 4, w.causal,
                                  None if kv_len is None else kv_len.tolist())
-    tiling = attnio.attn_query_tiling(w.d, w.causal)
+    if w.dtype == "bf16":
+        ranking = attnio.attn_tiling_enumerate(w.d, w.causal)
+        chosen = args.tiling if args.tiling >= 0 else next(e["compiled"] for e in ranking if e["compiled"] >= 0)
+        tiling = {**attnio.attn_tiling_get(chosen), "index": chosen,
+                  "model_pick": next(e["compiled"] for e in ranking if e["compiled"] >= 0)}
+    else:
+        tiling = attnio.attn_query_tiling(w.d, w.causal, "f32")
 
     for _ in range(args.warmup):
         fn(qd, kd, vd, causal=w.causal, kv_len=kvd, scale=w.scale, out=out)

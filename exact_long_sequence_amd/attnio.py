@@ -23,6 +23,7 @@ ATTN_OK = 0
 __all__ = ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd", "attn_bwd_noalloc",
            "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
            "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_fwd_fp8", "attn_strerror", "attn_version", "attn_query_tiling",
+           "attn_tiling_count", "attn_tiling_get", "attn_tiling_enumerate", "attn_io_bound_bytes", "attn_fwd_tiled",
            "attn_io_model", "library_path", "load_library"]
 
 
@@ -71,8 +72,19 @@ def load_library() -> ctypes.CDLL:
     lib.attn_version.argtypes = []
     lib.attn_version.restype = i32
     ip = ctypes.POINTER(ctypes.c_int)
-    lib.attn_query_tiling.argtypes = [i32, i32, ip, ip, ip, ip]
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.attn_query_tiling.argtypes = [i32, i32, i32, ip, ip, ip]
     lib.attn_query_tiling.restype = i32
+    lib.attn_tiling_count.argtypes = []
+    lib.attn_tiling_count.restype = i32
+    lib.attn_tiling_get.argtypes = [i32, vp]
+    lib.attn_tiling_get.restype = i32
+    lib.attn_tiling_enumerate.argtypes = [i32, i32, i32, vp, i32]
+    lib.attn_tiling_enumerate.restype = i32
+    lib.attn_io_bound_bytes.argtypes = [i32, i32, i32, i32, i32, i32, vp, dp, dp, dp]
+    lib.attn_io_bound_bytes.restype = i32
+    lib.attn_fwd_tiled.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32, vp]
+    lib.attn_fwd_tiled.restype = i32
     lib.attn_io_model.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(ctypes.c_double)]
     lib.attn_io_model.restype = i32
     _lib = lib
@@ -87,13 +99,101 @@ def attn_version() -> int:
     return int(load_library().attn_version())
 
 
-def attn_query_tiling(d: int, causal: bool = False) -> dict:
+_DTYPES = {"bf16": 0, "f32": 1, "fp8": 2}
+
+
+class AttnTiling(ctypes.Structure):
+    """attn_tiling of include/attnio.h."""
+    _fields_ = [(n, ctypes.c_int) for n in ("d", "BM", "BN", "stages", "waves", "lds_bytes", "wg_per_cu",
+                                            "qb", "pingpong", "rowsum_mfma")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class AttnTilingEval(ctypes.Structure):
+    """attn_tiling_eval of include/attnio.h."""
+    _fields_ = [("t", AttnTiling), ("compiled", ctypes.c_int), ("vgpr_estimate", ctypes.c_int),
+                ("vgpr_budget", ctypes.c_int)] + \
+               [(n, ctypes.c_double) for n in ("mfma_cycles", "valu_cycles", "issue_cycles_per_pair",
+                                               "lds_read_bytes_per_pair", "l2_to_lds_bytes_per_pair",
+                                               "beyond_l2_bytes_per_pair", "cycles_per_pair")] + \
+               [("bound", ctypes.c_int)]
+
+    def as_dict(self) -> dict:
+        d = {n: getattr(self, n) for n, _ in self._fields_ if n != "t"}
+        d["tiling"] = self.t.as_dict()
+        return d
+
+
+def attn_query_tiling(d: int, causal: bool = False, dtype: str = "bf16") -> dict:
+    """(BM, BN, stages) of the tiling the path of `dtype` uses for head size d."""
     lib = load_library()
-    vals = [ctypes.c_int(0) for _ in range(4)]
-    rc = lib.attn_query_tiling(int(d), int(bool(causal)), *[ctypes.byref(x) for x in vals])
+    vals = [ctypes.c_int(0) for _ in range(3)]
+    rc = lib.attn_query_tiling(int(d), _DTYPES[dtype], int(bool(causal)), *[ctypes.byref(x) for x in vals])
     if rc != ATTN_OK:
         raise RuntimeError(attn_strerror(rc))
-    return dict(zip(("BM", "BN", "stages", "waves"), (x.value for x in vals)))
+    return dict(zip(("BM", "BN", "stages"), (x.value for x in vals)))
+
+
+def attn_tiling_count() -> int:
+    return int(load_library().attn_tiling_count())
+
+
+def attn_tiling_get(index: int) -> dict:
+    t = AttnTiling()
+    rc = load_library().attn_tiling_get(int(index), ctypes.byref(t))
+    if rc != ATTN_OK:
+        raise RuntimeError(attn_strerror(rc))
+    return t.as_dict()
+
+
+def attn_tiling_enumerate(d: int, causal: bool = False, dtype: str = "bf16", max_out: int = 256) -> list:
+    """The model's feasible tilings for head size d, best first (list of dicts)."""
+    arr = (AttnTilingEval * max_out)()
+    n = load_library().attn_tiling_enumerate(int(d), _DTYPES[dtype], int(bool(causal)), arr, int(max_out))
+    if n < 0:
+        raise RuntimeError(attn_strerror(n))
+    return [arr[i].as_dict() for i in range(min(n, max_out))]
+
+
+def attn_io_bound_bytes(B: int, H: int, N: int, d: int, causal: bool, dtype: str = "bf16",
+                        kv_len_host=None) -> dict:
+    """T_min, T_LDS and T_L2 of one call (bytes; see include/attnio.h)."""
+    lib = load_library()
+    out = [ctypes.c_double(0) for _ in range(3)]
+    kv_ptr = None
+    if kv_len_host is not None:
+        arr = (ctypes.c_int32 * B)(*[int(x) for x in kv_len_host])
+        kv_ptr = ctypes.cast(arr, ctypes.c_void_p)
+    rc = lib.attn_io_bound_bytes(B, H, N, d, _DTYPES[dtype], int(bool(causal)), kv_ptr,
+                                 *[ctypes.byref(x) for x in out])
+    if rc != ATTN_OK:
+        raise RuntimeError(attn_strerror(rc))
+    return dict(zip(("t_min", "t_lds", "t_l2"), (x.value for x in out)))
+
+
+def attn_fwd_tiled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tiling_index: int, *,
+                   causal: bool = False, kv_len: Optional[torch.Tensor] = None,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """attn_fwd with the compiled tiling attn_tiling_get(tiling_index)."""
+    lib = load_library()
+    _check(q, k, v, torch.bfloat16)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    kv_len, kv_ptr = _kv_len_ptr(kv_len, B, q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_fwd_tiled(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d,
+                                float(scale), int(bool(causal)), kv_ptr, int(tiling_index), stream)
+    if rc != ATTN_OK:
+        raise RuntimeError(f"attn_fwd_tiled: {attn_strerror(rc)} (code {rc})")
+    return out
 
 
 def attn_io_model(B: int, H: int, N: int, d: int, elem_bytes: int, causal: bool,

@@ -19,8 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattnio.so")
-SOURCES = ["attnio_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
-           "attn_bwd_dq_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip", "attn_fwd_fp8.hip"]
+SOURCES = ["attnio_api.hip", "tile_model.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
+           "attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip",
+           "attn_fwd_fp8.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit; hipcc -O3
 # would otherwise form v_pk_{add,mul,fma}_f32 from plain float code.
@@ -62,7 +63,7 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="attnio_build_") as tmpdir:
         objs, cmds = [], []
         for src in SOURCES:
-            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
             cmds.append([cc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *inc, "-c",
                          os.path.join(CSRC, src), "-o", obj])

@@ -91,24 +91,17 @@ constexpr float kLazySumMax = 65536.f;  // a tile row sum above this moves the s
 // products with |V| > 1 overflow.
 constexpr float kSafeSumMax = 0x1p64f;
 
-// Where the row sums of P are formed: on the matrix core (next to the P x V
-// MFMAs, one tile late) or on the VALU (two-element dot products, in the
-// softmax).  Measured on MI355X: the same speed at d = 128 (the kernel runs at
-// a power-limited clock, and the two cost about the same energy), while at
-// d = 64 the VALU form lets two workgroups share a CU without register spills.
-#ifndef ATTNIO_RS_MFMA_D128
-#define ATTNIO_RS_MFMA_D128 1
-#endif
-#ifndef ATTNIO_RS_MFMA_D64
-#define ATTNIO_RS_MFMA_D64 0
-#endif
-constexpr bool rowsum_on_mfma(int d) {
-  return d == 128 ? ATTNIO_RS_MFMA_D128 != 0 : ATTNIO_RS_MFMA_D64 != 0;
-}
+// Where the row sums of P are formed is a property of each compiled tiling
+// (Tiling::rowsum_mfma below): on the matrix core (a 0/1 selection operand
+// times P, next to the P x V MFMAs, one tile late) or on the VALU (two-element
+// dot products, in the softmax).  The matrix-core form takes half a VALU
+// operation per score off the softmax but needs 4 + 4 QB more registers.
 
-template <int D, int BN, int WAVES, int NSTAGES>
+// Shape of one compiled tiling.  QB: 32-row query blocks per wave (a wave
+// owns 32 QB queries; each K or V operand read from LDS feeds QB MFMAs).
+template <int D, int BN, int WAVES, int NSTAGES, int QB = 1>
 struct Cfg {
-  static constexpr int BM = 32 * WAVES;                   // query rows per workgroup
+  static constexpr int BM = 32 * WAVES * QB;              // query rows per workgroup
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per row
@@ -117,10 +110,11 @@ struct Cfg {
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // K + V
   static constexpr int STAGES = NSTAGES;                 // (K, V) tile pairs in the LDS ring
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int LOADS = TILE_BYTES / 16 / THREADS;  // 16 B loads per thread per tensor
-  static_assert(TILE_BYTES % (16 * THREADS) == 0, "tile must split evenly over threads");
+  // the epilogue stages every output row of the workgroup in LDS
+  static constexpr int OUT_BYTES = BM * ROW_BYTES;
+  static constexpr int LDS_ALLOC = LDS_BYTES > OUT_BYTES ? LDS_BYTES : OUT_BYTES;
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
-  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
+  static_assert(LDS_ALLOC + 16 <= 160 * 1024, "gfx950 LDS is 160 KiB per CU");
 };
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row.  K rows are read
@@ -177,17 +171,18 @@ __device__ __forceinline__ void wait_dma_n() {
 // lone 32x32x16 chain at its full rate of one MFMA per 32 cycles even with
 // 1 KiB of LDS reads per MFMA, while reading 1-2 ahead (what the compiler
 // schedules on its own) costs about 40%.
-#ifndef ATTNIO_READ_AHEAD
-#define ATTNIO_READ_AHEAD 4
-#endif
-constexpr int kReadAhead = ATTNIO_READ_AHEAD;
+// Read-ahead distance in operand reads: 4 MFMAs at QB = 1; at QB = 2 each read
+// feeds two MFMAs, so 2 reads cover the same distance.
+template <int QB>
+constexpr int read_ahead() { return QB == 1 ? 4 : 2; }
 
-// One MFMA phase as a single stream of MFMAs:
-//   DO_PV: O^T (D x 32 queries) += V_tile^T P^T   ((BN/16) x (D/32) MFMAs)
+// One MFMA phase as a single stream of MFMAs, for the wave's QB query blocks:
+//   DO_PV: O^T (D x 32 queries) += V_tile^T P^T   ((BN/16) x (D/32) V operands)
 //          and, with DO_RS, the tile's row sums of P (BN/16 MFMAs, 16x16x32)
-//   DO_QK: S^T (BN keys x 32 queries) = K_tile Q^T ((D/16) x (BN/32) MFMAs)
-// in that order.  Each group of D/32 (resp. BN/32) consecutive MFMAs writes
-// independent accumulators, so dependent MFMAs are at least 3 apart.
+//   DO_QK: S^T (BN keys x 32 queries) = K_tile Q^T ((D/16) x (BN/32) K operands)
+// in that order.  Each operand read from LDS feeds QB MFMAs (one per query
+// block, different B operands).  Each group of QB * D/32 (resp. QB * BN/32)
+// consecutive MFMAs writes independent accumulators.
 //
 // Row sums on the matrix core.  The 16x16x32 instruction reads a B operand of
 // 32 k x 16 columns with lane 16g + j holding k = 8g .. 8g + 7 of column j, so
@@ -207,13 +202,14 @@ constexpr int kReadAhead = ATTNIO_READ_AHEAD;
 // the A-operand layout (d down the rows, keys along k).  The key order inside
 // each 16-key step matches the order in which the S^T accumulator holds the
 // same keys, so P needs no register shuffle.  The K operand is one 16-byte
-// read of row kb*32 + c.  A scheduling barrier after every MFMA pins the
-// read-ahead distance.
-template <class C, int D, int BN, bool DO_PV, bool DO_QK, bool DO_RS>
-__device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 (&pb)[BN / 16],
-                                            f32x16 (&acc)[D / 32], const bf16x8& sel, f32x4& lsum,
-                                            const char LDS_AS* kl, const bf16x8 (&qf)[D / 16],
-                                            f32x16 (&s)[BN / 32], int lane) {
+// read of row kb*32 + c.  A scheduling barrier after every operand's MFMAs
+// pins the read-ahead distance (counted in operand reads).
+template <class C, int D, int BN, int QB, int R, bool DO_PV, bool DO_QK, bool DO_RS>
+__device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 (&pb)[QB][BN / 16],
+                                            f32x16 (&acc)[QB][D / 32], const bf16x8& sel,
+                                            f32x4 (&lsum)[QB], const char LDS_AS* kl,
+                                            const bf16x8 (&qf)[QB][D / 16], f32x16 (&s)[QB][BN / 32],
+                                            int lane) {
   const int half = lane / 32, col = lane % 32;
   const int g = lane / 16;
   const int jr = (lane % 16) / 4;
@@ -221,7 +217,6 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
   constexpr int NPV = DO_PV ? (BN / 16) * (D / 32) : 0;
   constexpr int NQK = DO_QK ? (D / 16) * (BN / 32) : 0;
   constexpr int NM = NPV + NQK;
-  constexpr int R = kReadAhead;
   // Every operand address is the lane's base address of this tile XOR a
   // compile-time constant, plus an immediate row offset.  The swizzles are
   // XORs on the chunk index with a period that divides the row steps, and the
@@ -241,10 +236,7 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
   uint32_t vbase = (uint32_t)(uintptr_t)vl +
                          (uint32_t)(vrow * C::ROW_BYTES + ((((g % 2) * 2 + qq / 2) ^ swz_v<C>(vrow)) * 16) +
                                     (qq % 2) * 8);
-#ifndef ATTNIO_ADDR_REMAT
-#define ATTNIO_ADDR_REMAT 1
-#endif
-  if (ATTNIO_ADDR_REMAT) asm volatile("" : "+v"(kbase), "+v"(vbase));
+  asm volatile("" : "+v"(kbase), "+v"(vbase));
   auto read = [&](int m) __attribute__((always_inline)) {
     bf16x8 a;
     if (m < NPV) {
@@ -274,16 +266,24 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
     const bf16x8 a = ring[m % (R + 1)];
     if (m < NPV) {
       const int st = m / (D / 32), db = m % (D / 32);
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], acc[db], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][st], acc[qb][db], 0, 0, 0);
       if (DO_RS && db == D / 32 - 1) {
         const f32x4 zero4 = {};
-        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[st], st == 0 ? zero4 : lsum, 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[qb][st], st == 0 ? zero4 : lsum[qb],
+                                                             0, 0, 0);
       }
     } else {
       const int mq = m - NPV;
       const int ks = mq / (BN / 32), kb = mq % (BN / 32);
       const f32x16 zero = {};
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? zero : s[kb], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], ks == 0 ? zero : s[qb][kb], 0,
+                                                            0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -359,14 +359,31 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // ----------------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------------
-template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WG_PER_CU, bool KEYS_SNAKE, bool CAUSAL,
-          bool NEG_SCALE>
-__global__ __launch_bounds__(64 * WAVES, (WAVES / 4) * WG_PER_CU)
+
+// One compiled tiling: head size, keys per K/V tile, waves per workgroup,
+// 32-row query blocks per wave, LDS stages of the sequential form, loop form,
+// workgroups resident per CU (the residency the register budget and the
+// causal key order assume), causal key snake, row sums on the matrix core.
+template <int D_, int BN_, int WAVES_, int QB_, int STAGES_, bool PINGPONG_, int WG_PER_CU_, bool SNAKE_,
+          bool RS_MFMA_>
+struct Variant {
+  static constexpr int D = D_, BN = BN_, WAVES = WAVES_, QB = QB_;
+  static constexpr int STAGES = PINGPONG_ ? 2 : STAGES_;
+  static constexpr bool PINGPONG = PINGPONG_, KEYS_SNAKE = SNAKE_, RS_MFMA = RS_MFMA_;
+  static constexpr int WG_PER_CU = WG_PER_CU_;
+  using C = Cfg<D, BN, WAVES, STAGES, QB>;
+};
+
+template <class VT, bool CAUSAL, bool NEG_SCALE>
+__global__ __launch_bounds__(64 * VT::WAVES, (VT::WAVES / 4) * VT::WG_PER_CU)
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
                           const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
                           int N, float c, int n_qtiles) {
-  using C = Cfg<D, BN, WAVES, PINGPONG ? 2 : STAGES>;
+  constexpr int D = VT::D, BN = VT::BN, WAVES = VT::WAVES, QB = VT::QB, WG_PER_CU = VT::WG_PER_CU;
+  constexpr bool PINGPONG = VT::PINGPONG, KEYS_SNAKE = VT::KEYS_SNAKE, RS_MFMA = VT::RS_MFMA;
+  constexpr int R = read_ahead<QB>();
+  using C = typename VT::C;
   static_assert(!PINGPONG || WAVES % 2 == 0, "ping-pong needs two equal wave groups");
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   char LDS_AS* smem = (char LDS_AS*)smem_raw;
@@ -375,7 +392,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform
   const int lane = tid % 64;
   const int half = lane / 32;   // h
-  const int col = lane % 32;    // c: the query this lane owns
+  const int col = lane % 32;    // c: the query of each block this lane owns
 
   // ---- XCD-aware work assignment: (batch*head, query tile) ----
   // Workgroups are dispatched round-robin over the 8 XCDs (block x runs on
@@ -479,32 +496,36 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       }
     }
   };
-  const int qrow = q0 + wave * 32 + col;  // the query row this lane owns
+  const int qw0 = q0 + wave * 32 * QB;  // first query row of this wave; block qb: qw0 + 32 qb + col
   auto need_mask = [&](int t) __attribute__((always_inline)) {
     const int j0 = ktile(t) * BN;
-    return (j0 + BN > L) || (CAUSAL && (j0 + BN - 1 > q0 + wave * 32));
+    return (j0 + BN > L) || (CAUSAL && (j0 + BN - 1 > qw0));
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane (h, c) holds
-  //      Q[qrow][16*ks + 8*h .. +7] for every ks ----
+  //      Q[qw0 + 32 qb + c][16*ks + 8*h .. +7] for every qb, ks ----
   // Q is read once, so its loads are non-temporal: they do not push out of L2
   // the K/V tiles that the other query tiles of the head on this XCD are about
   // to read.  O, written once, leaves the same way from the epilogue (in whole
   // lines: a non-temporal store of 8-byte pieces would leave L2 unable to
   // merge them, measured at 4.8x the bytes written).
-  bf16x8 qf[D / 16];
-  {
+  bf16x8 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qw0 + 32 * qb + col;
     const int qrow_c = qrow < N ? qrow : N - 1;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = __builtin_nontemporal_load((const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 16 + half * 8));
+      qf[qb][ks] = __builtin_nontemporal_load((const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 16 + half * 8));
   }
   // Q operands must have arrived before the key loop: an empty asm that reads
   // them makes the compiler wait for their loads here, so that no wait for a
   // load of its own lands inside the loop, where the only vector-memory
   // operations are the tile DMAs (awaited explicitly before each barrier).
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[qb][ks]));
 
   // Selection operand of the row-sum MFMA (see mfma_stream): lane 16g + i
   // holds row i, k-group g of a 16 x 32 matrix that is 1 on rows 0 and 8 for
@@ -517,38 +538,37 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     for (int e = 0; e < 8; ++e) sel[e] = (__bf16)(one ? 1.f : 0.f);
   }
 
-  constexpr bool RS_MFMA = rowsum_on_mfma(D);
   // Ping-pong: the softmax wave issues the row-sum MFMAs of its previous P at
   // the start of its half step, while the MFMA wave of the SIMD waits for the
   // first LDS operands of the freshly published tiles (the matrix pipe is
   // otherwise idle there); the sequential form keeps them in the P x V stream.
   constexpr bool RS_STREAM = RS_MFMA && !PINGPONG;
-  f32x16 acc[D / 32];
-  float m_run;   // running shift, exp2 domain (scores * c)
-  float l_run;   // row sum of this lane's query: whole (RS_MFMA), else its 16 keys of each 32
-  f32x4 lsum;    // element 0: this query's sum of the last tile's P (matrix core)
-  bool bad;      // a tile's row sum was not finite: some probability overflowed
+  f32x16 acc[QB][D / 32];
+  float m_run[QB];   // running shift per query block, exp2 domain (scores * c)
+  float l_run[QB];   // row sum of this lane's query: whole (RS_MFMA), else its 16 keys of each 32
+  f32x4 lsum[QB];    // element 0: this query's sum of the last tile's P (matrix core)
+  bool bad;          // a tile's row sum exceeded the bound the accumulator can take
 
-  f32x16 s0[BN / 32];
-  bf16x8 pb[BN / 16];
+  f32x16 s0[QB][BN / 32];
+  bf16x8 pb[QB][BN / 16];
 
-  // Move the shift to the current row extremes of s0 where a row's extreme
-  // exceeds it by more than 2^TAU, rescaling acc and l.  The rescales here and
-  // in fold_sum are per-lane branches (executed under the lane mask, skipped
-  // when no lane needs them): as wave-uniform branches the compiler gave the
-  // two paths different accumulator registers and copied all 64 of them on
-  // the common path of every tile.
-  auto update_shift = [&]() __attribute__((always_inline)) {
-    const float m_tile = row_extreme<BN, NEG_SCALE>(s0) * c;
-    if (m_tile > m_run + kTauLog2) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+  // Move the shift of query block qb to the current row extremes of s0 where
+  // a row's extreme exceeds it by more than 2^TAU, rescaling acc and l.  The
+  // rescales here and in fold_sum are per-lane branches (executed under the
+  // lane mask, skipped when no lane needs them): as wave-uniform branches the
+  // compiler gave the two paths different accumulator registers and copied
+  // all of them on the common path of every tile.
+  auto update_shift = [&](int qb) __attribute__((always_inline)) {
+    const float m_tile = row_extreme<BN, NEG_SCALE>(s0[qb]) * c;
+    if (m_tile > m_run[qb] + kTauLog2) {
+      const float m_new = fmaxf(m_run[qb], m_tile);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      m_run[qb] = m_new;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      l_run[qb] *= alpha;
     }
   };
   // Row sums of the P held in pb (16x16x32 MFMAs with the selection operand).
@@ -556,7 +576,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const f32x4 zero4 = {};
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st)
-      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[st], st == 0 ? zero4 : lsum, 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[qb][st], st == 0 ? zero4 : lsum[qb], 0, 0, 0);
   };
   // Fold in the row sums of the previous tile (formed after its P x V).  The
   // shift is lazy: it is taken from the first tile that shows a row a visible
@@ -570,18 +592,21 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // recomputes its rows with the shift checked before every tile (the safe
   // pass below).
   auto fold_sum = [&]() __attribute__((always_inline)) {
-    const float rs = lsum[0];
-    bad = bad || !(rs <= kSafeSumMax);
-    l_run += rs;
-    if (rs > kLazySumMax && rs <= kSafeSumMax) {
-      const float mv = floorf(__builtin_amdgcn_logf(rs));
-      const float alpha = __builtin_amdgcn_exp2f(-mv);
-      m_run += mv;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+      const float rs = lsum[qb][0];
+      bad = bad || !(rs <= kSafeSumMax);
+      l_run[qb] += rs;
+      if (rs > kLazySumMax && rs <= kSafeSumMax) {
+        const float mv = floorf(__builtin_amdgcn_logf(rs));
+        const float alpha = __builtin_amdgcn_exp2f(-mv);
+        m_run[qb] += mv;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      l_run *= alpha;
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+        l_run[qb] *= alpha;
+      }
     }
   };
   // VALU part of tile t: fold the previous tile's row sums, mask, shift (first
@@ -592,19 +617,23 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   auto softmax_tile = [&](int t, auto safe_tag) __attribute__((always_inline)) {
     constexpr bool SAFE = decltype(safe_tag)::value;
     if (RS_MFMA) fold_sum();
-    if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0, ktile(t) * BN, L, qrow, half);
-    if (RS_MFMA) {
-      // per lane: the two lanes of a query (c, c + 32) share m_run, so the
-      // permlane32 swap in row_extreme only pairs active lanes
-      if (SAFE || m_run == -INFINITY) update_shift();
-      softmax_p<BN, false>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
-    } else {
-      float lt = softmax_p<BN, true>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
-      if (__builtin_amdgcn_ballot_w64(!(lt <= kLazySumMax) || m_run == -INFINITY) != 0) {
-        update_shift();
-        lt = softmax_p<BN, true>(s0, c, m_run == -INFINITY ? 0.f : m_run, pb);
+    const bool msk = need_mask(t);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (msk) mask_tile<BN, CAUSAL, NEG_SCALE>(s0[qb], ktile(t) * BN, L, qw0 + 32 * qb + col, half);
+      if (RS_MFMA) {
+        // per lane: the two lanes of a query (c, c + 32) share m_run, so the
+        // permlane32 swap in row_extreme only pairs active lanes
+        if (SAFE || m_run[qb] == -INFINITY) update_shift(qb);
+        softmax_p<BN, false>(s0[qb], c, m_run[qb] == -INFINITY ? 0.f : m_run[qb], pb[qb]);
+      } else {
+        float lt = softmax_p<BN, true>(s0[qb], c, m_run[qb] == -INFINITY ? 0.f : m_run[qb], pb[qb]);
+        if (__builtin_amdgcn_ballot_w64(!(lt <= kLazySumMax) || m_run[qb] == -INFINITY) != 0) {
+          update_shift(qb);
+          lt = softmax_p<BN, true>(s0[qb], c, m_run[qb] == -INFINITY ? 0.f : m_run[qb], pb[qb]);
+        }
+        l_run[qb] += lt;
       }
-      l_run += lt;
     }
   };
 
@@ -613,13 +642,16 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // edge and push the register count past the two-waves-per-SIMD limit).
   auto run_pass = [&](auto safe_tag) __attribute__((always_inline)) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  m_run = -INFINITY;
-  l_run = 0.f;
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) lsum[r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lsum[qb][r] = 0.f;
+  }
   bad = false;
 
   if constexpr (PINGPONG) {
@@ -627,7 +659,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // w + WAVES/2 share a SIMD.  Every wave runs the same straight loop
     // MFMA(t), barrier, VALU(t), barrier, with
     //   MFMA(t) = O += V(t-1)^T P(t-1)^T (t >= 1), then S(t) = K(t) Q^T (t < ntiles)
-    //   VALU(t) = [d = 128: row sums of P(t-1) on the matrix core,] softmax of tile t;
+    //   VALU(t) = [row sums of P(t-1) on the matrix core,] softmax of tile t;
     // group 1 passes one extra barrier first, which shifts it half a tile
     // behind group 0 (a barrier counts arrivals, not program locations), so on
     // each SIMD one group's MFMA stream runs under the other's softmax.  The
@@ -663,13 +695,19 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       // keep the softmax in this half step: without these uses the compiler
       // sinks the exponentials past the barrier, next to the P x V MFMAs
 #pragma unroll
-      for (int i = 0; i < BN / 16; ++i) asm volatile("" ::"v"(pb[i]));
-      asm volatile("" ::"v"(l_run));
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < BN / 16; ++i) asm volatile("" ::"v"(pb[qb][i]));
+        asm volatile("" ::"v"(l_run[qb]));
+      }
       if (grp == 0) wait_dma();
       __syncthreads();
     };
     if (ntiles > 0) {
-      issue(all_tag, 0, Kg, false, 0, kd(0));
+      // K(0) by every wave, or by group 0 when the tile is smaller than one
+      // 16-byte load per thread of the workgroup
+      if constexpr (C::TILE_BYTES % (16 * C::THREADS) == 0) issue(all_tag, 0, Kg, false, 0, kd(0));
+      else if (grp == 0) issue(half_tag, 0, Kg, false, 0, kd(0));
       wait_dma();
       __syncthreads();
       if (grp == 1) {
@@ -677,16 +715,16 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         __syncthreads();
       }
       step(0, safe_tag, [&]() __attribute__((always_inline)) {
-        mfma_stream<C, D, BN, false, true, false>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
+        mfma_stream<C, D, BN, QB, R, false, true, false>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
       });
       for (int t = 1; t < ntiles; ++t)
         step(t, safe_tag, [&]() __attribute__((always_inline)) {
-          mfma_stream<C, D, BN, true, true, false>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t), qf,
-                                                   s0, lane);
+          mfma_stream<C, D, BN, QB, R, true, true, false>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t),
+                                                          qf, s0, lane);
         });
       __builtin_amdgcn_s_setprio(2);
-      mfma_stream<C, D, BN, true, false, false>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem, qf, s0,
-                                                lane);
+      mfma_stream<C, D, BN, QB, R, true, false, false>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem, qf,
+                                                       s0, lane);
       __builtin_amdgcn_s_setprio(0);
       if (RS_MFMA) {
         rowsum_mfma();
@@ -698,7 +736,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // Sequential form over an LDS ring of STAGES (K, V) tile pairs: the DMAs of
     // tile t + STAGES - 1 are in flight while tile t is computed.
     constexpr int AHEAD = C::STAGES - 1;
-    constexpr int LOADS = C::TILE_BYTES / 16 / C::THREADS;
+    static_assert(C::TILE_BYTES % (16 * C::THREADS) == 0, "tile must split evenly over the threads");
+    constexpr int LOADS = C::TILE_BYTES / 16 / C::THREADS;  // 16 B loads per thread per tile
     std::integral_constant<int, WAVES> all_tag;
     auto sk = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t % C::STAGES) * C::STAGE_BYTES); };
     auto sv = [&](int t) __attribute__((always_inline)) { return sk(t) + (uint32_t)C::TILE_BYTES; };
@@ -716,9 +755,10 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         issue(all_tag, 0, Kg, false, t + AHEAD, sk(t + AHEAD));
         issue(all_tag, 0, Vg, true, t + AHEAD, sv(t + AHEAD));
       }
-      mfma_stream<C, D, BN, false, true, false>(smem, pb, acc, sel, lsum, smem + sk(t), qf, s0, lane);
+      mfma_stream<C, D, BN, QB, R, false, true, false>(smem, pb, acc, sel, lsum, smem + sk(t), qf, s0, lane);
       softmax_tile(t, safe_tag);
-      mfma_stream<C, D, BN, true, false, RS_STREAM>(smem + sv(t), pb, acc, sel, lsum, smem, qf, s0, lane);
+      mfma_stream<C, D, BN, QB, R, true, false, RS_STREAM>(smem + sv(t), pb, acc, sel, lsum, smem, qf, s0,
+                                                           lane);
       // tile t + 1 must have landed; the DMAs of tiles t + 2 .. t + AHEAD may
       // stay in flight (2 * LOADS instructions per tile and wave)
       if (more) wait_dma_n<(AHEAD - 1) * 2 * LOADS>();
@@ -731,7 +771,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // The fast pass; then a workgroup vote.  Every wave has finished the pass
   // (no DMA is in flight and no LDS tile is read after the barrier), so the
   // safe pass can reuse the ring.
-  int LDS_AS* vote = (int LDS_AS*)(smem + C::LDS_BYTES);
+  int LDS_AS* vote = (int LDS_AS*)(smem + C::LDS_ALLOC);
   if (tid == 0) *vote = 0;
   run_pass(std::false_type{});
   if (RS_MFMA) {  // the VALU row sum tests every tile before its P x V
@@ -741,53 +781,60 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   }
 
   // ---------------- epilogue: O = O^T / l ----------------
-  float l_tot = l_run;
-  if (!RS_MFMA) {
-    const u32x2 lp = swap_halves(l_run);
-    l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
-  }
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // log-sum-exp: sum_j 2^(c s_j) = 2^m_run * l, so ln(sum_j e^(scale s_j)) = (m_run + log2 l) ln 2
-  // (one 128-byte line per wave: the 32 lanes of half 0 write consecutive rows)
-  if (lse != nullptr && half == 0 && qrow < N)
-    __builtin_nontemporal_store(l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY,
-                                lse + (size_t)bh * N + qrow);
   // O leaves through LDS so that it can be written in whole lines with
   // non-temporal stores (streamed past L2, where the K/V tiles of the head's
-  // other query tiles stay).  Lane (h, c) holds 4-element pieces of row c; it
-  // writes them into this wave's 32 x ROW_BYTES slice of the (now idle) ring,
-  // 16-byte chunks XOR-swizzled by the row (spreads the 32 rows' equal
-  // columns over the banks); then each store instruction of the wave writes
-  // 1 KiB of whole rows, 16 contiguous bytes per lane.
+  // other query tiles stay).  Lane (h, c) holds 4-element pieces of row c of
+  // each block; it writes them into the block's 32 x ROW_BYTES slice of the
+  // (now idle) LDS, 16-byte chunks XOR-swizzled by the row (spreads the 32
+  // rows' equal columns over the banks); then each store instruction of the
+  // wave writes 1 KiB of whole rows, 16 contiguous bytes per lane.
   __syncthreads();  // every wave is past its last read of the K/V ring
-  static_assert(32 * C::ROW_BYTES * WAVES <= C::LDS_BYTES, "output staging must fit the ring");
-  char LDS_AS* ost = smem + wave * 32 * C::ROW_BYTES;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      bf16x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[db][a4 * 4 + e] * inv);
-      const int byte = (db * 32 + a4 * 8 + half * 4) * 2;  // within row c
-      const int ch = (byte / 16) ^ (col % C::CHUNKS);
-      *(bf16x4 LDS_AS*)(ost + col * C::ROW_BYTES + ch * 16 + byte % 16) = o;
+  for (int qb = 0; qb < QB; ++qb) {
+    float l_tot = l_run[qb];
+    if (!RS_MFMA) {
+      const u32x2 lp = swap_halves(l_run[qb]);
+      l_tot = __uint_as_float(lp[0]) + __uint_as_float(lp[1]);
     }
-  constexpr int ROWS_PER_STORE = 64 / C::CHUNKS;  // rows one 64-lane store covers
-  const int q_w = q0 + wave * 32;                 // first query row of this wave
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int qrow = qw0 + 32 * qb + col;
+    // log-sum-exp: sum_j 2^(c s_j) = 2^m_run * l, so ln(sum_j e^(scale s_j)) = (m_run + log2 l) ln 2
+    // (one 128-byte line per block: the 32 lanes of half 0 write consecutive rows)
+    if (lse != nullptr && half == 0 && qrow < N)
+      __builtin_nontemporal_store(l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY,
+                                  lse + (size_t)bh * N + qrow);
+    char LDS_AS* ost = smem + (wave * QB + qb) * 32 * C::ROW_BYTES;
 #pragma unroll
-  for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
-    const int row = i * ROWS_PER_STORE + lane / C::CHUNKS;
-    const int chunk = lane % C::CHUNKS;
-    const u32x4 v = *(const u32x4 LDS_AS*)(ost + row * C::ROW_BYTES + ((chunk ^ (row % C::CHUNKS)) * 16));
-    if (q_w + row < N)
-      __builtin_nontemporal_store(v, (u32x4*)(Os + (size_t)(q_w + row) * D + chunk * 8));
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[qb][db][a4 * 4 + e] * inv);
+        const int byte = (db * 32 + a4 * 8 + half * 4) * 2;  // within row c
+        const int ch = (byte / 16) ^ (col % C::CHUNKS);
+        *(bf16x4 LDS_AS*)(ost + col * C::ROW_BYTES + ch * 16 + byte % 16) = o;
+      }
+  }
+  constexpr int ROWS_PER_STORE = 64 / C::CHUNKS;  // rows one 64-lane store covers
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const char LDS_AS* ost = smem + (wave * QB + qb) * 32 * C::ROW_BYTES;
+    const int q_b = qw0 + 32 * qb;  // first query row of this block
+#pragma unroll
+    for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
+      const int row = i * ROWS_PER_STORE + lane / C::CHUNKS;
+      const int chunk = lane % C::CHUNKS;
+      const u32x4 v = *(const u32x4 LDS_AS*)(ost + row * C::ROW_BYTES + ((chunk ^ (row % C::CHUNKS)) * 16));
+      if (q_b + row < N)
+        __builtin_nontemporal_store(v, (u32x4*)(Os + (size_t)(q_b + row) * D + chunk * 8));
+    }
   }
 }
 
-template <int D, int BN, int WAVES, int STAGES, bool PINGPONG, int WPC, bool SNAKE, bool CAUSAL, bool NEG>
+template <class VT, bool CAUSAL, bool NEG>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  using C = Cfg<D, BN, WAVES, PINGPONG ? 2 : STAGES>;
+  using C = typename VT::C;
   const int n_qtiles = (a.N + C::BM - 1) / C::BM;
   const long long grid = (long long)a.B * a.H * n_qtiles;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -797,91 +844,78 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   // score maps to exp2(0) = 1 exactly: uniform weights, as for c = 0
   float c = a.scale * kLog2e;
   if (c == 0.f) c = FLT_MIN;
-  auto kern = attn_fwd_bf16_kernel<D, BN, WAVES, STAGES, PINGPONG, WPC, SNAKE, CAUSAL, NEG>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_BYTES + 16, stream,
+  auto kern = attn_fwd_bf16_kernel<VT, CAUSAL, NEG>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_ALLOC + 16, stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
                      a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
 }
 
-template <class P>
+template <class VT>
 hipError_t dispatch_mask(const FwdArgs& a, hipStream_t stream) {
-  constexpr int D = P::D, BN = P::BN, W = P::WAVES, ST = P::STAGES, WPC = P::WG_PER_CU;
-  constexpr bool PP = P::PINGPONG, SN = P::KEYS_SNAKE;
   const bool neg = a.scale < 0.f;
-  if (a.causal) return neg ? launch_t<D, BN, W, ST, PP, WPC, SN, true, true>(a, stream)
-                           : launch_t<D, BN, W, ST, PP, WPC, SN, true, false>(a, stream);
-  return neg ? launch_t<D, BN, W, ST, PP, WPC, SN, false, true>(a, stream)
-             : launch_t<D, BN, W, ST, PP, WPC, SN, false, false>(a, stream);
+  if (a.causal) return neg ? launch_t<VT, true, true>(a, stream) : launch_t<VT, true, false>(a, stream);
+  return neg ? launch_t<VT, false, true>(a, stream) : launch_t<VT, false, false>(a, stream);
 }
 
-// Tile shape and loop form per head size.  Measured on MI355X (causal,
-// N = 32768, d = 128): ping-pong with 8 waves and 128-key tiles is about 6%
-// faster than the 4-wave sequential form and reads 18% fewer bytes from
-// beyond L2 (256 instead of 128 resident query rows per workgroup).  The
-// macros let tuning builds select other shapes.
-#ifndef ATTNIO_PINGPONG
-#define ATTNIO_PINGPONG 1
-#endif
-#ifndef ATTNIO_BN_D128
-#define ATTNIO_BN_D128 (ATTNIO_PINGPONG ? 128 : 64)
-#endif
-#ifndef ATTNIO_BN_D64
-#define ATTNIO_BN_D64 64
-#endif
-#ifndef ATTNIO_STAGES
-#define ATTNIO_STAGES 2
-#endif
-// WG_PER_CU: workgroups resident per CU.  The kernel asks the compiler for
-// (WAVES / 4) * WG_PER_CU waves per SIMD (the register budget: 256 VGPRs for
-// one 8-wave workgroup per CU, 128 for two), and the causal key order and the host I/O
-// model assume that residency (d = 128: one workgroup, 128 KiB of LDS;
-// d = 64: WG_PER_CU workgroups of 32 KiB LDS each).
-// KEYS_SNAKE: causal generations alternate the key direction (see the kernel).
-#ifndef ATTNIO_WPC_D64
-#define ATTNIO_WPC_D64 2
-#endif
-#ifndef ATTNIO_SNAKE_D128
-#define ATTNIO_SNAKE_D128 1
-#endif
-#ifndef ATTNIO_SNAKE_D64
-#define ATTNIO_SNAKE_D64 1
-#endif
-template <int HD> struct Pick;
-template <> struct Pick<128> {
-  static constexpr int D = 128, BN = ATTNIO_BN_D128, WAVES = ATTNIO_PINGPONG ? 8 : 4;
-  static constexpr int STAGES = ATTNIO_STAGES;
-  static constexpr bool PINGPONG = ATTNIO_PINGPONG != 0;
-  static constexpr int WG_PER_CU = ATTNIO_PINGPONG ? 1 : 2;
-  static constexpr bool KEYS_SNAKE = ATTNIO_SNAKE_D128 != 0;
-};
-template <> struct Pick<64> {
-  static constexpr int D = 64, BN = ATTNIO_BN_D64, WAVES = ATTNIO_PINGPONG ? 8 : 4;
-  static constexpr int STAGES = ATTNIO_STAGES;
-  static constexpr bool PINGPONG = ATTNIO_PINGPONG != 0;
-  static constexpr int WG_PER_CU = ATTNIO_PINGPONG ? ATTNIO_WPC_D64 : 4;
-  static constexpr bool KEYS_SNAKE = ATTNIO_SNAKE_D64 != 0;
+// The compiled tilings.  Which one a call runs is decided on the host by the
+// I/O and issue model of the front end (it evaluates every feasible tiling and
+// takes the best compiled one); the set below holds that model's choices for
+// the long-sequence workloads plus their nearest neighbours, which the model
+// was checked against by measurement.
+//   d = 128: ping-pong, 8 waves x 32 queries, 128- or 64-key tiles, one
+//            256-row workgroup per CU; and the sequential 4-wave form at two
+//            128-row workgroups per CU.
+//   d = 64:  ping-pong, 8 waves x 64 queries (two blocks per wave), 64-key
+//            tiles, one 512-row workgroup per CU, row sums on the matrix core;
+//            16 waves x 32 queries, one 512-row workgroup per CU, VALU row
+//            sums; 8 waves x 32 queries at two 256-row workgroups per CU with
+//            VALU row sums; and 128-key tiles at one 256-row workgroup per CU.
+//                   D    BN  W  QB ST  PP     WPC SNAKE RS_MFMA
+using V128_PP128 = Variant<128, 128, 8, 1, 2, true, 1, true, true>;
+using V128_PP64 = Variant<128, 64, 8, 1, 2, true, 1, true, true>;
+using V128_SEQ64 = Variant<128, 64, 4, 1, 2, false, 2, true, true>;
+using V64_PP64_QB2 = Variant<64, 64, 8, 2, 2, true, 1, true, true>;
+using V64_PP64 = Variant<64, 64, 8, 1, 2, true, 2, true, false>;
+using V64_PP128 = Variant<64, 128, 8, 1, 2, true, 1, true, true>;
+using V64_PP64_W16 = Variant<64, 64, 16, 1, 2, true, 1, true, false>;
+
+template <class VT>
+constexpr Tiling tiling_of() {
+  using C = typename VT::C;
+  return Tiling{VT::D, C::BM, VT::BN, C::STAGES, VT::WAVES, C::LDS_ALLOC + 16, VT::WG_PER_CU, VT::QB,
+                VT::PINGPONG ? 1 : 0, VT::RS_MFMA ? 1 : 0};
+}
+
+struct Entry {
+  Tiling t;
+  hipError_t (*launch)(const FwdArgs&, hipStream_t);
 };
 
-template <class P>
-void fill_tiling(Tiling* t) {
-  using C = Cfg<P::D, P::BN, P::WAVES, P::PINGPONG ? 2 : P::STAGES>;
-  *t = {C::BM, P::BN, C::STAGES, P::WAVES, C::LDS_BYTES, P::WG_PER_CU};
-}
+const Entry kEntries[] = {
+    {tiling_of<V128_PP128>(), &dispatch_mask<V128_PP128>},
+    {tiling_of<V128_PP64>(), &dispatch_mask<V128_PP64>},
+    {tiling_of<V128_SEQ64>(), &dispatch_mask<V128_SEQ64>},
+    {tiling_of<V64_PP64_QB2>(), &dispatch_mask<V64_PP64_QB2>},
+    {tiling_of<V64_PP64>(), &dispatch_mask<V64_PP64>},
+    {tiling_of<V64_PP128>(), &dispatch_mask<V64_PP128>},
+    {tiling_of<V64_PP64_W16>(), &dispatch_mask<V64_PP64_W16>},
+};
+constexpr int kNumEntries = (int)(sizeof(kEntries) / sizeof(kEntries[0]));
 
 }  // namespace
 
-bool bf16_tiling(int d, int causal, Tiling* t) {
-  (void)causal;
-  if (d == 128) { fill_tiling<Pick<128>>(t); return true; }
-  if (d == 64) { fill_tiling<Pick<64>>(t); return true; }
-  return false;
+int bf16_variant_count() { return kNumEntries; }
+
+bool bf16_variant(int i, Tiling* t) {
+  if (i < 0 || i >= kNumEntries) return false;
+  *t = kEntries[i].t;
+  return true;
 }
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return dispatch_mask<Pick<128>>(a, stream);
-  if (a.d == 64) return dispatch_mask<Pick<64>>(a, stream);
-  return hipErrorInvalidValue;
+hipError_t launch_fwd_bf16(int variant, const FwdArgs& a, hipStream_t stream) {
+  if (variant < 0 || variant >= kNumEntries || kEntries[variant].t.d != a.d) return hipErrorInvalidValue;
+  return kEntries[variant].launch(a, stream);
 }
 
 }  // namespace attnio

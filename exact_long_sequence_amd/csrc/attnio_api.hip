@@ -74,10 +74,41 @@ int validate(const void* Q, const void* K, const void* V, void* O, int B, int H,
   return ATTN_OK;
 }
 
+// Under ATTNIO_LOG=1: the model's ranking for head size d, once per process.
+void log_tiling_choice(int d) {
+  static std::once_flag once[2];
+  std::call_once(once[d == 128 ? 0 : 1], [d] {
+    attnio::TileEval ev[256];
+    const int n = attnio::enumerate_tilings(d, ev, 256);
+    const int pick = attnio::chosen_variant(d);
+    fprintf(stderr, "[attnio] tiling model, d=%d: %d feasible tilings; best first:\n", d, n);
+    for (int i = 0; i < n && i < 6; ++i) {
+      const attnio::Tiling& t = ev[i].t;
+      fprintf(stderr,
+              "[attnio]   BM=%d BN=%d stages=%d waves=%d qb=%d wg/cu=%d %s rowsum=%s vgpr~%d/%d: "
+              "%.4f cyc/pair (issue %.4f, LDS %.1f B, L2->LDS %.2f B, beyond L2 %.4f B)%s\n",
+              t.BM, t.BN, t.stages, t.waves, t.qb, t.wg_per_cu, t.pingpong ? "ping-pong" : "sequential",
+              t.rowsum_mfma ? "mfma" : "valu", ev[i].vgpr_estimate, ev[i].vgpr_budget, ev[i].cycles_per_pair,
+              ev[i].issue_cycles_per_pair, ev[i].lds_read_bytes_per_pair, ev[i].l2_to_lds_bytes_per_pair,
+              ev[i].beyond_l2_bytes_per_pair, ev[i].compiled >= 0 ? " [compiled]" : "");
+    }
+    attnio::Tiling t{};
+    if (attnio::bf16_variant(pick, &t))
+      fprintf(stderr, "[attnio]   running compiled tiling %d: BM=%d BN=%d waves=%d qb=%d wg/cu=%d\n", pick,
+              t.BM, t.BN, t.waves, t.qb, t.wg_per_cu);
+  });
+}
+
 int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* lse, bool want_lse,
-        int B, int H, int N, int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+        int B, int H, int N, int d, float scale, int causal, const int32_t* kv_len, void* stream,
+        int variant = -1) {
   const int rc = validate(Q, K, V, O, B, H, N, d, scale, bf16 ? 2 : 4);
   if (rc != ATTN_OK) return rc;
+  if (bf16) {
+    if (variant < 0) variant = attnio::chosen_variant(d);
+    attnio::Tiling vt{};
+    if (!attnio::bf16_variant(variant, &vt) || vt.d != d) return ATTN_E_ARG;
+  }
   if (want_lse) {
     if (lse == nullptr) return ATTN_E_NULL;
     if (((uintptr_t)lse) & 3u) return ATTN_E_ALIGN;
@@ -92,14 +123,17 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   attnio::FwdArgs a{Q, K, V, O, kv_len, B, H, N, d, scale, causal ? 1 : 0, want_lse ? lse : nullptr};
   if (log_enabled()) {
     attnio::Tiling t{};
-    if (bf16 && attnio::bf16_tiling(d, causal, &t))
-      fprintf(stderr, "[attnio] bf16 B=%d H=%d N=%d d=%d causal=%d kv_len=%s BM=%d BN=%d stages=%d waves=%d lds=%d\n",
-              B, H, N, d, causal, kv_len ? "dev" : "none", t.BM, t.BN, t.stages, t.waves, t.lds_bytes);
-    else
+    if (bf16 && attnio::bf16_variant(variant, &t)) {
+      log_tiling_choice(d);
+      fprintf(stderr, "[attnio] bf16 B=%d H=%d N=%d d=%d causal=%d kv_len=%s tiling %d: BM=%d BN=%d "
+              "stages=%d waves=%d qb=%d wg/cu=%d lds=%d\n", B, H, N, d, causal, kv_len ? "dev" : "none",
+              variant, t.BM, t.BN, t.stages, t.waves, t.qb, t.wg_per_cu, t.lds_bytes);
+    } else {
       fprintf(stderr, "[attnio] f32 B=%d H=%d N=%d d=%d causal=%d kv_len=%s\n", B, H, N, d, causal,
               kv_len ? "dev" : "none");
+    }
   }
-  const hipError_t e = bf16 ? attnio::launch_fwd_bf16(a, (hipStream_t)stream)
+  const hipError_t e = bf16 ? attnio::launch_fwd_bf16(variant, a, (hipStream_t)stream)
                             : attnio::launch_fwd_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) {
     if (log_enabled()) fprintf(stderr, "[attnio] launch failed: %s\n", hipGetErrorString(e));
@@ -108,12 +142,6 @@ int run(bool bf16, const void* Q, const void* K, const void* V, void* O, float* 
   return ATTN_OK;
 }
 
-// number of (query, visible key) pairs of one (b, h) slice
-double pair_count(long long N, long long L, bool causal) {
-  if (!causal) return (double)N * (double)L;
-  // sum_i min(i + 1, L) = L(L+1)/2 + (N - L) L
-  return (double)L * (double)(L + 1) / 2.0 + (double)(N - L) * (double)L;
-}
 
 // ---------------------------------------------------------------------------
 // Backward scratch without allocation.  attn_bwd_noalloc keeps the backward's
@@ -363,13 +391,75 @@ const char* attn_strerror(int code) {
 
 int attn_version(void) { return kVersion; }
 
-int attn_query_tiling(int d, int causal, int* BM, int* BN, int* stages, int* waves) {
-  attnio::Tiling t{};
-  if (!attnio::bf16_tiling(d, causal, &t)) return ATTN_E_HEAD_DIM;
+int attn_tiling_count(void) { return attnio::bf16_variant_count(); }
+
+int attn_tiling_get(int index, attn_tiling* out) {
+  if (!out) return ATTN_E_NULL;
+  if (!attnio::bf16_variant(index, out)) return ATTN_E_ARG;
+  return ATTN_OK;
+}
+
+int attn_fwd_tiled(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* kv_len, int tiling_index, void* stream) {
+  if (tiling_index < 0 || tiling_index >= attnio::bf16_variant_count()) return ATTN_E_ARG;
+  return run(true, Q, K, V, O, nullptr, false, B, H, N, d, scale, causal, kv_len, stream, tiling_index);
+}
+
+int attn_tiling_enumerate(int d, int dtype, int causal, attn_tiling_eval* out, int max_out) {
+  (void)causal;
+  if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_E_ARG;
+  if (!out && max_out > 0) return ATTN_E_NULL;
+  attnio::TileEval ev[256];
+  const int n = attnio::enumerate_tilings(d, ev, 256);
+  for (int i = 0; i < n && i < max_out && i < 256; ++i) out[i] = ev[i];
+  return n;
+}
+
+namespace {
+// The tiling of the path of element type dtype for head size d.
+int path_tiling(int d, int dtype, attn_tiling* t) {
+  if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
+  *t = attn_tiling{};
+  t->d = d;
+  switch (dtype) {
+    case ATTN_DTYPE_BF16:
+      return attnio::bf16_variant(attnio::chosen_variant(d), t) ? ATTN_OK : ATTN_E_HEAD_DIM;
+    case ATTN_DTYPE_F32:
+      // 16 queries x 16 key lanes per 256-thread workgroup, 64-key tiles in LDS
+      t->BM = 16; t->BN = 64; t->stages = 1; t->waves = 4; t->qb = 1; t->wg_per_cu = 1;
+      t->lds_bytes = (16 + 2 * 64) * (d + 4) * 4;  // Q, K and V tiles, rows padded by 16 bytes
+      return ATTN_OK;
+    case ATTN_DTYPE_FP8:
+      // 4 waves x 32 queries, 128-key E4M3 tiles, two stages, two workgroups per CU
+      t->BM = 128; t->BN = 128; t->stages = 2; t->waves = 4; t->qb = 1; t->wg_per_cu = 2;
+      t->lds_bytes = 2 * 2 * 128 * d; t->rowsum_mfma = 1;
+      return ATTN_OK;
+    default:
+      return ATTN_E_ARG;
+  }
+}
+}  // namespace
+
+int attn_query_tiling(int d, int dtype, int causal, int* BM, int* BN, int* stages) {
+  (void)causal;
+  attn_tiling t{};
+  const int rc = path_tiling(d, dtype, &t);
+  if (rc != ATTN_OK) return rc;
   if (BM) *BM = t.BM;
   if (BN) *BN = t.BN;
   if (stages) *stages = t.stages;
-  if (waves) *waves = t.waves;
+  return ATTN_OK;
+}
+
+int attn_io_bound_bytes(int B, int H, int N, int d, int dtype, int causal, const int32_t* kv_len_host,
+                        double* t_min, double* t_lds, double* t_l2) {
+  attn_tiling t{};
+  const int rc = path_tiling(d, dtype, &t);
+  if (rc != ATTN_OK) return rc;
+  if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
+  const int elem = dtype == ATTN_DTYPE_F32 ? 4 : dtype == ATTN_DTYPE_FP8 ? 1 : 2;
+  attnio::io_bytes(t, B, H, N, d, elem, causal != 0, kv_len_host, t_min, t_lds, t_l2, nullptr);
   return ATTN_OK;
 }
 
@@ -380,53 +470,9 @@ int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
   if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
   if (elem_bytes != 2 && elem_bytes != 4) return ATTN_E_ARG;
   attnio::Tiling t{};
-  attnio::bf16_tiling(d, causal, &t);
-  const double row = (double)d * elem_bytes;
-  const long long BM = t.BM, BN = t.BN;
-  const long long nqt = (N + BM - 1) / BM;
-  // query tiles of one head run together on one XCD (32 CUs), `resident` at
-  // a time; each such generation streams the keys it needs through L2 once
-  const long long resident = 32LL * (t.wg_per_cu > 0 ? t.wg_per_cu : 1);
-  double t_min = 4.0 * B, t_lds = 0, t_l2 = 0, pairs = 0;
-  for (int b = 0; b < B; ++b) {
-    long long L = N;
-    if (kv_len_host) {
-      L = kv_len_host[b];
-      L = L < 0 ? 0 : (L > N ? N : L);
-    }
-    const double p = pair_count(N, L, causal != 0);
-    for (int h = 0; h < H; ++h) {
-      pairs += p;
-      t_min += row * (2.0 * N + 2.0 * L);
-      t_l2 += row * 2.0 * N;  // Q read and O written once
-      for (long long qt = 0; qt < nqt; ++qt) {
-        long long kend = L;
-        if (causal) kend = kend < (qt + 1) * BM ? kend : ((qt + 1) * BM < N ? (qt + 1) * BM : N);
-        const long long tiles = (kend + BN - 1) / BN;
-        t_lds += row * (double)BM + 2.0 * row * (double)(tiles * BN);
-      }
-      // one generation = `resident` query tiles running together; K/V of the
-      // keys that generation needs come from beyond L2 once per generation,
-      // assuming its workgroups walk the keys in step.  Causal generations
-      // alternate the key direction, so each one after the first starts on
-      // keys the previous one ended on: up to one L2 (4 MiB per XCD) of them
-      // is reused.
-      const double l2_keys = 4.0 * 1024.0 * 1024.0 / (2.0 * row);
-      for (long long g0 = 0; g0 < nqt; g0 += resident) {
-        // causal tiles run longest first: generation g covers the highest
-        // remaining query tiles, so it needs keys up to its first tile's end
-        const long long top = causal ? nqt - g0 : nqt;
-        long long kend = L;
-        if (causal) kend = kend < top * BM ? kend : (top * BM < N ? top * BM : N);
-        double keys = (double)kend;
-        if (causal && g0 > 0) keys -= (l2_keys < keys ? l2_keys : keys);
-        t_l2 += 2.0 * row * keys;
-      }
-    }
-  }
-  out[0] = t_min;
-  out[1] = t_lds;
-  out[2] = t_l2;
+  attnio::bf16_variant(attnio::chosen_variant(d), &t);
+  double pairs = 0;
+  attnio::io_bytes(t, B, H, N, d, elem_bytes, causal != 0, kv_len_host, &out[0], &out[1], &out[2], &pairs);
   out[3] = 4.0 * d * pairs;
   out[4] = pairs;
   return ATTN_OK;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/attnio.h"
+
 namespace attnio {
 
 // Launch parameters common to both precisions.  All pointers are device
@@ -20,15 +22,22 @@ struct FwdArgs {
   float* lse;             // device float[B, H, N] or nullptr (log-sum-exp side output)
 };
 
-// Tile configuration of the bf16 streaming kernel for head size d.
-struct Tiling {
-  int BM;      // query rows resident per workgroup
-  int BN;      // keys per streamed K/V tile
-  int stages;  // K/V LDS buffers
-  int waves;   // wavefronts per workgroup (32 query rows each)
-  int lds_bytes;
-  int wg_per_cu;  // workgroups resident per CU (register and LDS bound)
-};
+// One tile configuration of the bf16 streaming kernel, and the model's
+// evaluation of one (the public structs of include/attnio.h).
+using Tiling = attn_tiling;
+using TileEval = attn_tiling_eval;
+
+// Host-side tiling model (tile_model.cpp).
+int vgpr_estimate(int d, int BN, int qb, int rowsum_mfma);
+bool tiling_fits(const Tiling& t, int* vgpr_est, int* vgpr_budget);
+void price_tiling(TileEval* e);
+// every feasible tiling for head size d, best first; returns the count
+int enumerate_tilings(int d, TileEval* out, int max_out);
+// compiled variant the forward runs for head size d (the best compiled one)
+int chosen_variant(int d);
+// T_min, T_LDS, T_L2 and visible pairs of one call with tiling t
+void io_bytes(const Tiling& t, int B, int H, int N, int d, int elem, int causal,
+              const int32_t* kv_len_host, double* t_min, double* t_lds, double* t_l2, double* pairs);
 
 // Backward launch parameters (device pointers validated by the front end).
 struct BwdArgs {
@@ -88,7 +97,10 @@ struct Fp8Args {
   float q_descale, k_descale, v_descale;
 };
 
-bool bf16_tiling(int d, int causal, Tiling* t);
+// The compiled bf16 forward tilings: count, description of entry i, launch of
+// entry i (its head size must be a.d).
+int bf16_variant_count();
+bool bf16_variant(int i, Tiling* t);
 hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int rows_cached_sweeps(int N);
 hipError_t launch_stream_rows(const RowArgs& a, hipStream_t stream);
@@ -102,7 +114,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 // c = scale * log2(e)).
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* ws_d, const float* ws_l, int NP,
                               float c, hipStream_t stream);
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_bf16(int variant, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace attnio

@@ -204,11 +204,91 @@ const char* attn_strerror(int code);
 /* Library version, as major*10000 + minor*100 + patch. */
 int attn_version(void);
 
-/* Tile configuration the bf16 path uses for head size d (1 = causal): rows of
- * the resident query tile (BM), keys per streamed K/V tile (BN), K/V LDS stages
- * and waves per workgroup.  Host only.  Returns 0 or ATTN_E_HEAD_DIM.  Any
+/* Element types of the tiling and I/O-model queries. */
+enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F32 = 1, ATTN_DTYPE_FP8 = 2 };
+
+/* One tiling of the bf16 streamed forward ("From Attention Graph to
+ * FlashAttention - A Memory-Centric Compilation Approach in AICF", section 5:
+ * tile size, reduction axis, residency and streaming order of the streaming
+ * region).  A workgroup keeps BM = 32 * waves * qb query rows resident in
+ * registers and streams K/V tiles of BN keys through LDS. */
+typedef struct attn_tiling {
+  int d;            /* head size */
+  int BM;           /* query rows resident per workgroup */
+  int BN;           /* keys per streamed K/V tile */
+  int stages;       /* K/V tile pairs buffered in LDS */
+  int waves;        /* wavefronts per workgroup */
+  int lds_bytes;    /* LDS per workgroup */
+  int wg_per_cu;    /* workgroups resident per CU */
+  int qb;           /* 32-row query blocks per wave */
+  int pingpong;     /* 1: two wave groups alternate the MFMA and softmax phases */
+  int rowsum_mfma;  /* 1: row sums of P formed on the matrix core */
+} attn_tiling;
+
+/* Number of bf16 forward tilings compiled into the library, and the shape of
+ * entry `index` (0 <= index < count).  Host only; attn_tiling_get returns 0,
+ * ATTN_E_NULL or ATTN_E_ARG. */
+int attn_tiling_count(void);
+int attn_tiling_get(int index, attn_tiling* out);
+
+/* attn_fwd with an explicit compiled tiling (an index of attn_tiling_get whose
+ * d matches) instead of the one the I/O model picks; same contract and
+ * results up to rounding order (bitwise equal where the tiling is the picked
+ * one).  For measuring the tilings against each other.  ATTN_E_ARG if the
+ * index is out of range or its head size differs from d. */
+int attn_fwd_tiled(const void* Q, const void* K, const void* V, void* O,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* kv_len, int tiling_index, void* stream);
+
+/* The I/O and issue model's view of one tiling: whether it fits a gfx950 CU
+ * (160 KiB of LDS, 512 registers per SIMD lane shared by the SIMD's waves) and
+ * what it costs per (query, key) pair at each level of the memory hierarchy
+ * ("IO-Aware Algorithms", How it works: the tiled product's traffic
+ * 2MNK -> 2MNK/S, and the roofline of each memory tier). */
+typedef struct attn_tiling_eval {
+  attn_tiling t;
+  int compiled;                     /* attn_tiling_get index, or -1 if not built */
+  int vgpr_estimate;                /* registers per lane the tiling needs (estimate) */
+  int vgpr_budget;                  /* registers per lane its residency leaves */
+  double mfma_cycles;               /* MFMA phase per wave per key tile (cycles) */
+  double valu_cycles;               /* softmax phase per wave per key tile (cycles) */
+  double issue_cycles_per_pair;     /* per CU, from the phase model */
+  double lds_read_bytes_per_pair;   /* K/V operand reads from LDS */
+  double l2_to_lds_bytes_per_pair;  /* K/V tile fetches into LDS: 4d / BM */
+  double beyond_l2_bytes_per_pair;  /* K/V fetched past L2: 4d / (rows resident per XCD) */
+  double cycles_per_pair;           /* predicted: the costliest of the four levels */
+  int bound;                        /* which: 0 issue, 1 LDS, 2 L2->LDS, 3 beyond L2 */
+} attn_tiling_eval;
+
+/* Enumerate every tiling of the bf16 forward for head size d that fits a CU,
+ * priced by the model and sorted best first (ties within 1% go to fewer bytes
+ * beyond L2, then into LDS, then to wider key tiles); the forward runs the
+ * first compiled one.  Writes up to max_out entries, returns how many tilings
+ * fit (or a negative code: ATTN_E_HEAD_DIM, ATTN_E_ARG for dtype other than
+ * bf16, ATTN_E_NULL).  causal does not change the per-pair prices.  Host only. */
+int attn_tiling_enumerate(int d, int dtype, int causal, attn_tiling_eval* out, int max_out);
+
+/* Tile configuration the path of element type `dtype` (ATTN_DTYPE_*) uses for
+ * head size d (causal: 1 = causal mask): rows of the resident query tile (BM),
+ * keys per streamed K/V tile (BN) and K/V LDS stages.  For bf16 it is the
+ * compiled tiling the I/O model picks ("I/O Analysis is All You Need",
+ * abstract: I/O-optimal tiling and scheduling); fp32 and fp8 have one tiling
+ * each.  Host only.  Returns 0, ATTN_E_HEAD_DIM or ATTN_E_ARG (dtype).  Any
  * output pointer may be NULL. */
-int attn_query_tiling(int d, int causal, int* BM, int* BN, int* stages, int* waves);
+int attn_query_tiling(int d, int dtype, int causal, int* BM, int* BN, int* stages);
+
+/* Analytic I/O bounds of one call of the path of element type `dtype`, host
+ * only (kv_len_host: a HOST int32[B] or NULL), in bytes:
+ *   t_min  the compulsory HBM traffic, Q, K, V read once and O written once
+ *          (keys past kv_len never read), plus 4*B bytes of kv_len: the
+ *          Theta(N d) I/O of the fused form ("IO-Aware Algorithms", How it
+ *          works), the bound measured traffic is compared with;
+ *   t_lds  bytes streamed into LDS by the tiling attn_query_tiling reports
+ *          (2MNK -> 2MNK/S with S = BM, same page);
+ *   t_l2   predicted bytes fetched beyond L2 (as out[2] of attn_io_model).
+ * Any output pointer may be NULL.  Returns 0 or a negative code. */
+int attn_io_bound_bytes(int B, int H, int N, int d, int dtype, int causal,
+                        const int32_t* kv_len_host, double* t_min, double* t_lds, double* t_l2);
 
 /* I/O model of one call (host only; kv_len_host is a HOST int32[B] or NULL).
  * Fills, in bytes:

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     assert {"attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_f32_lse", "attn_bwd",
             "attn_bwd_workspace_bytes", "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
             "stream_softmax", "stream_layernorm", "stream_rows_cached", "attn_fwd_fp8", "attn_strerror",
-            "attn_version",
+            "attn_version", "attn_bwd_noalloc", "attn_tiling_count", "attn_tiling_get", "attn_fwd_tiled",
+            "attn_tiling_enumerate", "attn_io_bound_bytes",
             "attn_query_tiling", "attn_io_model"} <= names
 
 
@@ -50,15 +51,69 @@ def test_strerror_and_version(lib):
     assert "unknown" in attnio.attn_strerror(-99)
 
 
-def test_query_tiling():
+def test_query_tiling(lib):
     for d in (64, 128):
-        t = attnio.attn_query_tiling(d, False)
-        assert t["BM"] % 32 == 0 and t["BN"] % 32 == 0 and t["stages"] >= 2
-        assert t["BM"] == 32 * t["waves"]
-        # K and V stages of BN x d bf16 rows fit the 160 KiB LDS of a gfx950 CU
-        assert t["stages"] * 2 * t["BN"] * d * 2 <= 160 * 1024
+        for causal in (False, True):
+            t = attnio.attn_query_tiling(d, causal)
+            assert t["BM"] % 32 == 0 and t["BN"] % 32 == 0 and t["stages"] >= 2
+            # K and V stages of BN x d bf16 rows fit the 160 KiB LDS of a gfx950 CU
+            assert t["stages"] * 2 * t["BN"] * d * 2 <= 160 * 1024
+        # the fp32 and fp8 paths have one tiling each
+        assert attnio.attn_query_tiling(d, False, "f32") == {"BM": 16, "BN": 64, "stages": 1}
+        assert attnio.attn_query_tiling(d, True, "fp8") == {"BM": 128, "BN": 128, "stages": 2}
     with pytest.raises(RuntimeError):
         attnio.attn_query_tiling(96, False)
+    # the raw call: NULL outputs allowed, bad dtype and head size refused
+    assert lib.attn_query_tiling(128, 0, 1, None, None, None) == 0
+    assert lib.attn_query_tiling(128, 7, 1, None, None, None) == -8
+    assert lib.attn_query_tiling(80, 0, 1, None, None, None) == -2
+
+
+def test_tiling_table_and_explicit_tiling_errors(lib):
+    n = attnio.attn_tiling_count()
+    assert n >= 2
+    seen = set()
+    for i in range(n):
+        t = attnio.attn_tiling_get(i)
+        assert t["BM"] == 32 * t["waves"] * t["qb"] and t["d"] in (64, 128)
+        assert t["wg_per_cu"] * t["lds_bytes"] <= 160 * 1024
+        key = tuple(sorted(t.items()))
+        assert key not in seen
+        seen.add(key)
+    with pytest.raises(RuntimeError):
+        attnio.attn_tiling_get(n)
+    assert lib.attn_tiling_get(0, None) == -1
+
+    def call(index, d=64):
+        return lib.attn_fwd_tiled(0x1000, 0x2000000, 0x4000000, 0x6000000, 1, 1, 16, d,
+                                  ctypes.c_float(0.125), 0, None, index, None)
+    assert call(-1) == -8 and call(n) == -8
+    wrong_d = next(i for i in range(n) if attnio.attn_tiling_get(i)["d"] != 64)
+    assert call(wrong_d, d=64) == -8            # the tiling's head size must match
+    assert lib.attn_fwd_tiled(None, 0x2000000, 0x4000000, 0x6000000, 1, 1, 16, 64,
+                              ctypes.c_float(0.125), 0, None, 0, None) == -1
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        right_d = next(i for i in range(n) if attnio.attn_tiling_get(i)["d"] == 64)
+        assert call(right_d) == -6
+
+
+def test_io_bound_bytes_matches_closed_forms(lib):
+    B, H, N, d = 2, 3, 1000, 128
+    for dtype, e in (("bf16", 2), ("f32", 4), ("fp8", 1)):
+        io = attnio.attn_io_bound_bytes(B, H, N, d, False, dtype)
+        assert io["t_min"] == 4 * B + e * d * B * H * (2 * N + 2 * N)
+        assert io["t_lds"] >= io["t_min"] - 4 * B and io["t_l2"] >= io["t_min"] - 4 * B
+    p = attnio.attn_io_bound_bytes(2, 1, 64, 64, True, "bf16", [10, 64])
+    assert p["t_min"] == 8 + 2 * 64 * (2 * 64 + 2 * 10) + 2 * 64 * (2 * 64 + 2 * 64)
+    # bf16 figures are those of attn_io_model for the same call
+    m = attnio.attn_io_model(B, H, N, d, 2, True)
+    io = attnio.attn_io_bound_bytes(B, H, N, d, True)
+    assert (io["t_min"], io["t_lds"], io["t_l2"]) == (m["t_min"], m["t_lds"], m["t_l2"])
+    assert lib.attn_io_bound_bytes(1, 1, 16, 64, 0, 0, None, None, None, None) == 0
+    assert lib.attn_io_bound_bytes(0, 1, 16, 64, 0, 0, None, None, None, None) == -3
+    assert lib.attn_io_bound_bytes(1, 1, 16, 96, 0, 0, None, None, None, None) == -2
+    assert lib.attn_io_bound_bytes(1, 1, 16, 64, 9, 0, None, None, None, None) == -8
 
 
 def _call(lib, name, q=0x1000, k=0x2000000, v=0x4000000, o=0x6000000, B=1, H=1, N=16, d=64,
