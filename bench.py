@@ -19,6 +19,7 @@ a bounded row sample on the host cores (which also checks those rows).
   python bench.py --mode fp8 [--workload NAME]   # the workload's shape with E4M3 inputs
   python bench.py --mode tilings --all-workloads  # every compiled tiling vs the I/O model's pick
   python bench.py --copy-calib BYTES   # plain device copy, for counter calibration
+  python bench.py --read-calib BYTES [--read-repeats 8]   # one buffer read repeatedly
 
 In --mode bwd one step is one attn_bwd call (its three kernels) from the
 forward's O and log-sum-exp, which are computed before the timed region; the
@@ -81,6 +82,22 @@ def copy_calibration(nbytes: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+
+
+def read_calibration(nbytes: int, repeats: int) -> None:
+    """Read one device buffer of nbytes `repeats` times (one reduction kernel
+    each).  With nbytes well above the 4 MiB per-XCD L2 and well below the
+    256 MiB Infinity Cache, FETCH_SIZE per dispatch tells whether the counter
+    sees L2 misses that the Infinity Cache serves (every dispatch reads
+    nbytes) or only DRAM reads (the repeats read almost nothing)."""
+    import torch
+    src = torch.ones(nbytes // 4, device="cuda:0", dtype=torch.float32)
+    torch.cuda.synchronize()
+    acc = torch.zeros((), device="cuda:0")
+    for _ in range(repeats):
+        acc += src.sum()
+    torch.cuda.synchronize()
+    print(json.dumps({"read_calibration_bytes": nbytes, "repeats": repeats, "sum": float(acc)}), flush=True)
 
 
 def cpu_baseline(w, q, k, v, kv_len, out, budget_s: float):
@@ -517,6 +534,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calib", type=int, default=0, help="run a plain copy of this many bytes")
+    ap.add_argument("--read-calib", type=int, default=0,
+                    help="read a device buffer of this many bytes --read-repeats times")
+    ap.add_argument("--read-repeats", type=int, default=8)
     ap.add_argument("--mode", choices=("fwd", "bwd", "unfused", "rows", "fp8", "tilings"), default="fwd")
     ap.add_argument("--reps", type=int, default=4, help="--mode tilings: interleaved rounds per tiling")
     ap.add_argument("--all-workloads", action="store_true", help="--mode tilings: every bf16 workload")
@@ -536,6 +556,9 @@ def main() -> int:
 
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+        return 0
+    if args.read_calib:
+        read_calibration(args.read_calib, args.read_repeats)
         return 0
 
     from exact_long_sequence_amd import attnio

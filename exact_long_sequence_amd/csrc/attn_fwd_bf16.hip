@@ -365,11 +365,17 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // workgroups resident per CU (the residency the register budget and the
 // causal key order assume), causal key snake, row sums on the matrix core.
 template <int D_, int BN_, int WAVES_, int QB_, int STAGES_, bool PINGPONG_, int WG_PER_CU_, bool SNAKE_,
-          bool RS_MFMA_>
+          bool RS_MFMA_, bool RS_IN_STREAM_ = false>
 struct Variant {
   static constexpr int D = D_, BN = BN_, WAVES = WAVES_, QB = QB_;
   static constexpr int STAGES = PINGPONG_ ? 2 : STAGES_;
   static constexpr bool PINGPONG = PINGPONG_, KEYS_SNAKE = SNAKE_, RS_MFMA = RS_MFMA_;
+  // where the matrix-core row sums are issued in the ping-pong form: by the
+  // MFMA wave, next to the P x V MFMAs of its phase, or (false) by the
+  // softmax wave at the start of its half step, in the window where the MFMA
+  // wave waits for its first LDS operands (the sequential form always puts
+  // them in the P x V stream)
+  static constexpr bool RS_IN_STREAM = RS_MFMA_ && (RS_IN_STREAM_ || !PINGPONG_);
   static constexpr int WG_PER_CU = WG_PER_CU_;
   using C = Cfg<D, BN, WAVES, STAGES, QB>;
 };
@@ -538,11 +544,12 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     for (int e = 0; e < 8; ++e) sel[e] = (__bf16)(one ? 1.f : 0.f);
   }
 
-  // Ping-pong: the softmax wave issues the row-sum MFMAs of its previous P at
-  // the start of its half step, while the MFMA wave of the SIMD waits for the
-  // first LDS operands of the freshly published tiles (the matrix pipe is
-  // otherwise idle there); the sequential form keeps them in the P x V stream.
-  constexpr bool RS_STREAM = RS_MFMA && !PINGPONG;
+  // Row sums on the matrix core are issued either in the P x V stream of the
+  // MFMA phase or, in the ping-pong form, by the softmax wave at the start of
+  // its half step, while the MFMA wave of the SIMD waits for the first LDS
+  // operands of the freshly published tiles (the matrix pipe is otherwise
+  // idle there, as long as that wait outlasts the row-sum MFMAs).
+  constexpr bool RS_STREAM = VT::RS_IN_STREAM;
   f32x16 acc[QB][D / 32];
   float m_run[QB];   // running shift per query block, exp2 domain (scores * c)
   float l_run[QB];   // row sum of this lane's query: whole (RS_MFMA), else its 16 keys of each 32
@@ -688,7 +695,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       __builtin_amdgcn_s_setprio(0);
       if (grp == 1) wait_dma();
       __syncthreads();
-      if (RS_MFMA && t > 0) rowsum_mfma();  // P(t - 1), still in pb
+      if (RS_MFMA && !RS_STREAM && t > 0) rowsum_mfma();  // P(t - 1), still in pb
       if (grp == 1) issue_step(t + 1);
       else issue(half_tag, 0, Vg, true, t, vd(t));
       softmax_tile(t, st_tag);
@@ -719,15 +726,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       });
       for (int t = 1; t < ntiles; ++t)
         step(t, safe_tag, [&]() __attribute__((always_inline)) {
-          mfma_stream<C, D, BN, QB, R, true, true, false>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t),
-                                                          qf, s0, lane);
+          mfma_stream<C, D, BN, QB, R, true, true, RS_STREAM>(smem + vd(t - 1), pb, acc, sel, lsum,
+                                                              smem + kd(t), qf, s0, lane);
         });
       __builtin_amdgcn_s_setprio(2);
-      mfma_stream<C, D, BN, QB, R, true, false, false>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem, qf,
-                                                       s0, lane);
+      mfma_stream<C, D, BN, QB, R, true, false, RS_STREAM>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem,
+                                                           qf, s0, lane);
       __builtin_amdgcn_s_setprio(0);
       if (RS_MFMA) {
-        rowsum_mfma();
+        if (!RS_STREAM) rowsum_mfma();
         fold_sum();
       }
       if (grp == 0) __syncthreads();  // group 1's last VALU barrier
@@ -879,12 +886,14 @@ using V64_PP64_QB2 = Variant<64, 64, 8, 2, 2, true, 1, true, true>;
 using V64_PP64 = Variant<64, 64, 8, 1, 2, true, 2, true, false>;
 using V64_PP128 = Variant<64, 128, 8, 1, 2, true, 1, true, true>;
 using V64_PP64_W16 = Variant<64, 64, 16, 1, 2, true, 1, true, false>;
+using V64_PP64_QB2_RSS = Variant<64, 64, 8, 2, 2, true, 1, true, true, true>;
+using V128_PP128_RSS = Variant<128, 128, 8, 1, 2, true, 1, true, true, true>;
 
 template <class VT>
 constexpr Tiling tiling_of() {
   using C = typename VT::C;
   return Tiling{VT::D, C::BM, VT::BN, C::STAGES, VT::WAVES, C::LDS_ALLOC + 16, VT::WG_PER_CU, VT::QB,
-                VT::PINGPONG ? 1 : 0, VT::RS_MFMA ? 1 : 0};
+                VT::PINGPONG ? 1 : 0, VT::RS_MFMA ? 1 : 0, VT::RS_IN_STREAM ? 1 : 0};
 }
 
 struct Entry {
@@ -900,6 +909,8 @@ const Entry kEntries[] = {
     {tiling_of<V64_PP64>(), &dispatch_mask<V64_PP64>},
     {tiling_of<V64_PP128>(), &dispatch_mask<V64_PP128>},
     {tiling_of<V64_PP64_W16>(), &dispatch_mask<V64_PP64_W16>},
+    {tiling_of<V64_PP64_QB2_RSS>(), &dispatch_mask<V64_PP64_QB2_RSS>},
+    {tiling_of<V128_PP128_RSS>(), &dispatch_mask<V128_PP128_RSS>},
 };
 constexpr int kNumEntries = (int)(sizeof(kEntries) / sizeof(kEntries[0]));
 

@@ -47,9 +47,8 @@
 // per-wave timestamps in instrumented builds of the kernel):
 //   MFMA work   M = 32 per 32x32x16 MFMA + 16 per 16x16x32 row-sum MFMA
 //                   + 120 waiting for the first LDS operands of the phase;
-//   softmax     S = 4 per VALU instruction + 10 per row-sum MFMA issued from
-//                   the softmax wave + DMA bytes / 64 B/clk (the CU's load
-//                   path), in solo-rate cycles; VALU instructions per tile =
+//   softmax     S = 4 per VALU instruction + DMA bytes / 64 B/clk (the CU's
+//                   load path), in solo-rate cycles; VALU instructions per tile =
 //                   scores per lane x 2.5 + 26 + 10 (qb - 1), plus, with the
 //                   row sum on the VALU, half a dot2 per score weighted by
 //                   0.59 / 0.37 (the measured rates of the other VALU work and
@@ -133,17 +132,28 @@ void price_tiling(TileEval* e) {
   // Per phase, the MFMA pipe is busy M_k cycles; the softmax work S_k (in
   // solo-rate cycles) runs at rate rho while the pipe is busy and at full rate
   // after it: phase time = M_k + max(0, S_k - rho M_k).
-  const double M = 32.0 * (n_pv + n_qk) + 16.0 * n_rs + kPhaseStartCycles;
   double round, pairs;
   if (t.pingpong) {
     const double k = t.waves / 8.0 * wpc;  // waves per SIMD in each phase
+    // Row sums issued by the softmax wave use the matrix pipe while the MFMA
+    // wave waits for its first LDS operands (about 32 cycles per operand read
+    // ahead), at no cost to either wave.  If they do not fit that wait they
+    // queue behind the MFMA stream, and the in-order softmax wave cannot
+    // start its VALU work until that stream ends: no overlap.  (Measured: at
+    // 4 reads ahead the softmax wave's placement is 2% faster than the
+    // stream's at d = 128; at 2 reads ahead, QB = 2, 1.8% slower at d = 64.)
+    const bool by_softmax = t.rowsum_mfma && !t.rowsum_in_stream;
+    const bool fits = 16.0 * n_rs <= 32.0 * read_ahead(t.qb);
+    const double M = 32.0 * (n_pv + n_qk) + (by_softmax ? 0.0 : 16.0 * n_rs) + kPhaseStartCycles;
     // per half step each workgroup's softmax group issues one tile's DMA (K or V)
-    const double S = k * (vinst * 4.0 + 10.0 * n_rs) + wpc * tile_bytes / kDmaBytesPerClk;
+    const double S = k * vinst * 4.0 + wpc * tile_bytes / kDmaBytesPerClk;
     e->mfma_cycles = M;
     e->valu_cycles = S / k;
-    round = 2.0 * (k * M + std::max(0.0, S - kRho * k * M));
+    const double overlap = (by_softmax && !fits) ? 0.0 : kRho;
+    round = 2.0 * (k * M + std::max(0.0, S - overlap * k * M));
     pairs = 2.0 * k * qb * 32.0 * BN;
   } else {
+    const double M = 32.0 * (n_pv + n_qk) + 16.0 * n_rs + kPhaseStartCycles;
     const double n = t.waves / 4.0 * wpc;  // waves sharing a SIMD
     // every wave runs both phases; the CU's waves issue both tiles (K and V)
     // of every workgroup, and the tile barrier costs kBarrierCycles
@@ -194,7 +204,7 @@ int compiled_index(const Tiling& t) {
     bf16_variant(i, &c);
     if (c.d == t.d && c.BM == t.BM && c.BN == t.BN && c.stages == t.stages && c.waves == t.waves &&
         c.wg_per_cu == t.wg_per_cu && c.qb == t.qb && c.pingpong == t.pingpong &&
-        c.rowsum_mfma == t.rowsum_mfma)
+        c.rowsum_mfma == t.rowsum_mfma && c.rowsum_in_stream == t.rowsum_in_stream)
       return i;
   }
   return -1;
@@ -208,7 +218,7 @@ int enumerate_tilings(int d, TileEval* out, int max_out) {
   static const int kBN[] = {32, 64, 128, 256};
   static const int kStages[] = {2, 3, 4};
   static const int kWPC[] = {1, 2, 3, 4};
-  TileEval all[3 * 2 * 4 * 3 * 4 * 2 * 2];
+  TileEval all[3 * 2 * 4 * 3 * 4 * 2 * 3];
   int n = 0;
   for (int w : kWaves)
     for (int qb : kQB)
@@ -216,7 +226,8 @@ int enumerate_tilings(int d, TileEval* out, int max_out) {
         for (int st : kStages)
           for (int wpc : kWPC)
             for (int pp = 0; pp < 2; ++pp)
-              for (int rs = 0; rs < 2; ++rs) {
+              for (int rs = 0; rs < 3; ++rs) {  // VALU; matrix core in the stream; by the softmax wave
+                if (rs == 2 && !pp) continue;
                 TileEval e{};
                 Tiling& t = e.t;
                 t.d = d;
@@ -227,7 +238,8 @@ int enumerate_tilings(int d, TileEval* out, int max_out) {
                 t.qb = qb;
                 t.wg_per_cu = wpc;
                 t.pingpong = pp;
-                t.rowsum_mfma = rs;
+                t.rowsum_mfma = rs > 0;
+                t.rowsum_in_stream = rs == 1;
                 const int ring = st * 2 * bn * d * 2, outb = t.BM * d * 2;
                 t.lds_bytes = std::max(ring, outb) + 16;
                 if (!tiling_fits(t, &e.vgpr_estimate, &e.vgpr_budget)) continue;

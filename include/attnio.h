@@ -223,6 +223,9 @@ typedef struct attn_tiling {
   int qb;           /* 32-row query blocks per wave */
   int pingpong;     /* 1: two wave groups alternate the MFMA and softmax phases */
   int rowsum_mfma;  /* 1: row sums of P formed on the matrix core */
+  int rowsum_in_stream; /* 1: those row-sum MFMAs issued in the P x V stream of the
+                           MFMA phase; 0 (ping-pong only): by the softmax wave at
+                           the start of its half step */
 } attn_tiling;
 
 /* Number of bf16 forward tilings compiled into the library, and the shape of

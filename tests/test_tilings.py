@@ -34,7 +34,7 @@ def _ids():
     out = []
     for i, t in _tilings():
         out.append(f"{i}-d{t['d']}-BM{t['BM']}-BN{t['BN']}-qb{t['qb']}-wpc{t['wg_per_cu']}"
-                   f"-{'pp' if t['pingpong'] else 'seq'}-{'rsm' if t['rowsum_mfma'] else 'rsv'}")
+                   f"-{'pp' if t['pingpong'] else 'seq'}-{'rsv' if not t['rowsum_mfma'] else ('rss' if t['rowsum_in_stream'] else 'rsw')}")
     return out
 
 
