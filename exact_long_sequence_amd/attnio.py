@@ -15,7 +15,10 @@ from typing import Optional
 
 import torch  # imported first so that libattnio.so binds to torch's HIP runtime
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libattnio.so")
+# ATTNIO_LIB names another build of the same library (the LDS-poison debug
+# build, for instance); it must exist, there is no fallback either way.
+_LIB_PATH = os.environ.get("ATTNIO_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
+                                                         "libattnio.so")
 _lib = None
 
 ATTN_OK = 0

@@ -3,7 +3,7 @@
 Each translation unit is compiled to an object of its own (in parallel, into a
 temporary directory), then the objects are linked into one shared library.
 
-Usage:  python -m exact_long_sequence_amd.build
+Usage:  python -m exact_long_sequence_amd.build [--debug-poison]
 """
 from __future__ import annotations
 
@@ -19,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattnio.so")
+POISON_LIB_PATH = os.path.join(LIB_DIR, "libattnio_poison.so")
 SOURCES = ["attnio_api.hip", "tile_model.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
            "attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip",
            "attn_fwd_fp8.hip"]
@@ -56,26 +57,31 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[:3])} ...")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, debug_poison: bool = False) -> str:
+    """Build libattnio.so; with debug_poison, the LDS-poison debug build
+    libattnio_poison.so instead (every K/V ring buffer NaN-filled as soon as
+    the ring protocol frees it; for checking that protocol, not for use)."""
     os.makedirs(LIB_DIR, exist_ok=True)
     cc = hipcc()
     inc = ["-I", os.path.join(ROOT, "include")]
+    defs = ["-DATTNIO_DEBUG_POISON=1"] if debug_poison else []
+    lib_path = POISON_LIB_PATH if debug_poison else LIB_PATH
     with tempfile.TemporaryDirectory(prefix="attnio_build_") as tmpdir:
         objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
-            cmds.append([cc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *inc, "-c",
+            cmds.append([cc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *defs, *inc, "-c",
                          os.path.join(CSRC, src), "-o", obj])
         workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
         with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
-        tmp = LIB_PATH + ".tmp"
+        tmp = lib_path + ".tmp"
         _run([cc, *HIPCC_FLAGS, "-shared", *objs, "-o", tmp], verbose)
-        os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, debug_poison="--debug-poison" in sys.argv[1:]))

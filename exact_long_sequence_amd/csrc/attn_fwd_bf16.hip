@@ -152,6 +152,27 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Debug build (ATTNIO_DEBUG_POISON=1): every K/V buffer of the LDS ring is
+// filled with bf16 NaNs as soon as the ring protocol lets it be overwritten,
+// before the DMA that refills it, so that a wave reading a buffer outside the
+// half steps the protocol gives it turns the output into NaNs.  Off in the
+// product build.
+#ifndef ATTNIO_DEBUG_POISON
+#define ATTNIO_DEBUG_POISON 0
+#endif
+constexpr bool kPoison = ATTNIO_DEBUG_POISON != 0;
+
+// NaN-fill `bytes` of LDS from byte address `lds` by `nthreads` threads
+// (thread index `t` among them), then wait for the writes to land so that a
+// DMA issued next by the same wave cannot be overtaken by them.
+__device__ __forceinline__ void poison_lds(uint32_t lds, int bytes, int nthreads, int t) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  for (int o = t * 16; o < bytes; o += nthreads * 16)
+    *(u32x4_t __attribute__((address_space(3)))*)(uintptr_t)(lds + (uint32_t)o) = nan4;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // wait until at most N tile DMAs of this wave are still in flight
 template <int N>
 __device__ __forceinline__ void wait_dma_n() {
@@ -696,6 +717,14 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       if (grp == 1) wait_dma();
       __syncthreads();
       if (RS_MFMA && !RS_STREAM && t > 0) rowsum_mfma();  // P(t - 1), still in pb
+      if (kPoison && grp == 1) {
+        // group 1, softmax(t): V(t - 1) was last read in the previous half step
+        // (group 1's P x V of it) and its buffer is refilled with V(t + 1)
+        // next half step; K(t)'s buffer gets K(t + 2) now
+        const int gt = tid - 64 * (WAVES / 2);
+        if (t >= 1) poison_lds(lds_base + vd(t + 1), C::TILE_BYTES, 64 * (WAVES / 2), gt);
+        if (t + 2 < ntiles) poison_lds(lds_base + kd(t + 2), C::TILE_BYTES, 64 * (WAVES / 2), gt);
+      }
       if (grp == 1) issue_step(t + 1);
       else issue(half_tag, 0, Vg, true, t, vd(t));
       softmax_tile(t, st_tag);
@@ -758,6 +787,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const bool more = t + AHEAD < ntiles;
+      // tile t - 1's slot: last read before the barrier that ended step t - 1
+      if (kPoison && more) poison_lds(lds_base + sk(t + AHEAD), C::STAGE_BYTES, C::THREADS, tid);
       if (more) {
         issue(all_tag, 0, Kg, false, t + AHEAD, sk(t + AHEAD));
         issue(all_tag, 0, Vg, true, t + AHEAD, sv(t + AHEAD));

@@ -43,6 +43,20 @@ bool current_device_is_gfx950() {
   return g_dev_ok[dev] == 1;
 }
 
+// B, H, N >= 1 and B*H*N*d < 2^31, tested without forming a product that could
+// overflow (each partial product stays below 2^31 before the next factor,
+// itself below 2^31, multiplies it).
+bool shape_ok(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return false;
+  const long long lim = 1LL << 31;
+  long long p = B;
+  for (long long f : {(long long)H, (long long)N, (long long)d}) {
+    p *= f;
+    if (p >= lim) return false;
+  }
+  return true;
+}
+
 // hipGetLastError() returns and clears the calling thread's last HIP error.
 // Called once the arguments are accepted and before anything is enqueued, so
 // that the status read after the launches names those launches only, not an
@@ -64,9 +78,8 @@ int validate(const void* Q, const void* K, const void* V, void* O, int B, int H,
              float scale, int elem) {
   if (!Q || !K || !V || !O) return ATTN_E_NULL;
   if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
-  if (B < 1 || H < 1 || N < 1) return ATTN_E_SHAPE;
+  if (!shape_ok(B, H, N, d)) return ATTN_E_SHAPE;
   const long long total = (long long)B * H * N * d;
-  if (total >= (1LL << 31)) return ATTN_E_SHAPE;
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return ATTN_E_ALIGN;
   const size_t bytes = (size_t)total * elem;
   if (overlaps(O, Q, bytes) || overlaps(O, K, bytes) || overlaps(O, V, bytes)) return ATTN_E_ALIAS;
@@ -310,7 +323,7 @@ int attn_fwd_fp8(const void* Q, const void* K, const void* V, void* O, int B, in
                  const int32_t* kv_len, void* stream) {
   if (!Q || !K || !V || !O) return ATTN_E_NULL;
   if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
-  if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
+  if (!shape_ok(B, H, N, d)) return ATTN_E_SHAPE;
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u) return ATTN_E_ALIGN;
   if (!std::isfinite(scale)) return ATTN_E_ARG;
   for (float s : {q_descale, k_descale, v_descale})
@@ -457,7 +470,7 @@ int attn_io_bound_bytes(int B, int H, int N, int d, int dtype, int causal, const
   attn_tiling t{};
   const int rc = path_tiling(d, dtype, &t);
   if (rc != ATTN_OK) return rc;
-  if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
+  if (!shape_ok(B, H, N, d)) return ATTN_E_SHAPE;
   const int elem = dtype == ATTN_DTYPE_F32 ? 4 : dtype == ATTN_DTYPE_FP8 ? 1 : 2;
   attnio::io_bytes(t, B, H, N, d, elem, causal != 0, kv_len_host, t_min, t_lds, t_l2, nullptr);
   return ATTN_OK;
@@ -467,7 +480,7 @@ int attn_io_model(int B, int H, int N, int d, int elem_bytes, int causal,
                   const int32_t* kv_len_host, double out[5]) {
   if (!out) return ATTN_E_NULL;
   if (d != 64 && d != 128) return ATTN_E_HEAD_DIM;
-  if (B < 1 || H < 1 || N < 1 || (long long)B * H * N * d >= (1LL << 31)) return ATTN_E_SHAPE;
+  if (!shape_ok(B, H, N, d)) return ATTN_E_SHAPE;
   if (elem_bytes != 2 && elem_bytes != 4) return ATTN_E_ARG;
   attnio::Tiling t{};
   attnio::bf16_variant(attnio::chosen_variant(d), &t);
