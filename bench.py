@@ -37,6 +37,13 @@ import re
 import sys
 import time
 
+# BLAS threads of the CPU oracle leg, set before numpy is first imported (torch
+# imports it): every host core this process may run on, unless the caller or
+# the machine already fixed a count.
+_HOST_THREADS = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, _HOST_THREADS)
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -70,6 +77,48 @@ def committed_traffic(w):
     if not (m_sha and m_b) or m_sha.group(1) != kernel_source_digest():
         return None
     return float(m_b.group(1))
+
+
+# The pages' own figures for this method, quoted as context only (no hardware,
+# precision or workload is given for either on the pages).
+PAGE_CONTEXT = {
+    "attenio_speedup_over_prior_solutions": {
+        "value": "1.6x-8.8x", "hardware": "not stated",
+        "source": "I/O Analysis is All You Need: An I/O Analysis for Long-Sequence Attention, abstract"},
+    "flashattention_speedup_over_native_pytorch": {
+        "value": "about 6x", "hardware": "not stated",
+        "source": "Neural Circuit Diagrams abstract"},
+}
+
+
+def committed_counters(w, ms: float):
+    """Issue and utilization figures of workload w from the committed
+    rocprofv3 summaries, when they were taken on the current kernel source:
+    MFMA pipe busy, other VALU instructions per MFMA, LDS bank-conflict cycles
+    per LDS-active cycle, the clock the kernel ran at, and the HBM bytes of
+    the counter summary divided by this run's time."""
+    stem = counter_summary_path(w)[:-len("_counters.md")]
+    out = {}
+    util = stem + "_utilization.md"
+    if w.dtype == "bf16" and os.path.exists(util):
+        text = open(util).read()
+        m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+        if m_sha and m_sha.group(1) == kernel_source_digest():
+            def num(pat):
+                m = re.search(pat, text)
+                return float(m.group(1)) if m else None
+            out["mfma_pipe_busy"] = num(r"MFMA pipe busy: .* = ([0-9.]+)")
+            out["valu_per_mfma"] = num(r"other VALU instructions per MFMA: .* = ([0-9.]+)")
+            conf = re.search(r"LDS bank conflict cycles / LDS active cycles: ([0-9.e+]+) / ([0-9.e+]+)", text)
+            out["lds_bank_conflict_rate"] = float(conf.group(1)) / float(conf.group(2)) if conf else None
+            out["clock_ghz"] = num(r"clock during the kernel: .* = ([0-9.]+) GHz")
+            out["source"] = os.path.relpath(util, ROOT)
+    traffic = committed_traffic(w)
+    if traffic is not None:
+        out["hbm_bytes"] = traffic
+        out["achieved_hbm_GBs"] = traffic / (ms * 1e-3) / 1e9
+        out["hbm_frac_of_peak"] = out["achieved_hbm_GBs"] / HBM_PEAK_GBS
+    return out or None
 
 
 def copy_calibration(nbytes: int) -> None:
@@ -646,6 +695,8 @@ def main() -> int:
             "hbm_peak_GBs": HBM_PEAK_GBS,
         },
         "tiling": tiling,
+        "counters": committed_counters(w, ms),
+        "context": PAGE_CONTEXT,
         "kernel_source_sha256_16": kernel_source_digest(),
     }
     if not args.no_cpu_baseline:

@@ -280,7 +280,8 @@ void io_bytes(const Tiling& t, int B, int H, int N, int d, int elem, int causal,
   // query tiles of one head run together on one XCD (32 CUs), `resident` at
   // a time; each such generation streams the keys it needs through L2 once
   const long long resident = 32LL * (t.wg_per_cu > 0 ? t.wg_per_cu : 1);
-  double t_min = 4.0 * B, t_lds = 0, t_l2 = 0, pairs = 0;
+  // the int32 key-padding lengths are read only when the call has them
+  double t_min = kv_len_host ? 4.0 * B : 0.0, t_lds = 0, t_l2 = 0, pairs = 0;
   for (int b = 0; b < B; ++b) {
     long long L = N;
     if (kv_len_host) {

@@ -283,7 +283,8 @@ int attn_query_tiling(int d, int dtype, int causal, int* BM, int* BN, int* stage
 /* Analytic I/O bounds of one call of the path of element type `dtype`, host
  * only (kv_len_host: a HOST int32[B] or NULL), in bytes:
  *   t_min  the compulsory HBM traffic, Q, K, V read once and O written once
- *          (keys past kv_len never read), plus 4*B bytes of kv_len: the
+ *          (keys past kv_len never read), plus 4*B bytes of kv_len when
+ *          kv_len_host is given: the
  *          Theta(N d) I/O of the fused form ("IO-Aware Algorithms", How it
  *          works), the bound measured traffic is compared with;
  *   t_lds  bytes streamed into LDS by the tiling attn_query_tiling reports
@@ -296,7 +297,8 @@ int attn_io_bound_bytes(int B, int H, int N, int d, int dtype, int causal,
 /* I/O model of one call (host only; kv_len_host is a HOST int32[B] or NULL).
  * Fills, in bytes:
  *   out[0] t_min   compulsory HBM traffic: Q, K, V read once, O written once
- *                  (keys past kv_len are never read), plus 4*B bytes of kv_len;
+ *                  (keys past kv_len are never read), plus 4*B bytes of
+ *                  kv_len when kv_len_host is given;
  *   out[1] t_lds   bytes streamed into LDS by the chosen tiling (Q once per
  *                  query tile, K/V once per query tile for every key tile the
  *                  tile visits) -- the L2->LDS traffic of the tall-skinny
