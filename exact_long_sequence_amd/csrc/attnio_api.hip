@@ -11,7 +11,7 @@
 
 #include <mutex>
 
-#include "../../include/attnio.h"
+#include "attnio.h"
 #include "kernels.h"
 
 namespace {
@@ -439,9 +439,9 @@ int path_tiling(int d, int dtype, attn_tiling* t) {
     case ATTN_DTYPE_BF16:
       return attnio::bf16_variant(attnio::chosen_variant(d), t) ? ATTN_OK : ATTN_E_HEAD_DIM;
     case ATTN_DTYPE_F32:
-      // 16 queries x 16 key lanes per 256-thread workgroup, 64-key tiles in LDS
-      t->BM = 16; t->BN = 64; t->stages = 1; t->waves = 4; t->qb = 1; t->wg_per_cu = 1;
-      t->lds_bytes = (16 + 2 * 64) * (d + 4) * 4;  // Q, K and V tiles, rows padded by 16 bytes
+      // 8 queries x 32 key lanes per 256-thread workgroup, 64-key tiles in LDS
+      t->BM = 8; t->BN = 64; t->stages = 1; t->waves = 4; t->qb = 1; t->wg_per_cu = 1;
+      t->lds_bytes = (8 + 2 * 64) * (d + 4) * 4;  // Q, K and V tiles, rows padded by 16 bytes
       return ATTN_OK;
     case ATTN_DTYPE_FP8:
       // 4 waves x 32 queries, 128-key E4M3 tiles, two stages, two workgroups per CU

@@ -59,7 +59,7 @@ def test_query_tiling(lib):
             # K and V stages of BN x d bf16 rows fit the 160 KiB LDS of a gfx950 CU
             assert t["stages"] * 2 * t["BN"] * d * 2 <= 160 * 1024
         # the fp32 and fp8 paths have one tiling each
-        assert attnio.attn_query_tiling(d, False, "f32") == {"BM": 16, "BN": 64, "stages": 1}
+        assert attnio.attn_query_tiling(d, False, "f32") == {"BM": 8, "BN": 64, "stages": 1}
         assert attnio.attn_query_tiling(d, True, "fp8") == {"BM": 128, "BN": 128, "stages": 2}
     with pytest.raises(RuntimeError):
         attnio.attn_query_tiling(96, False)
