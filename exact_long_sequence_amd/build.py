@@ -21,7 +21,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libattnio.so")
 POISON_LIB_PATH = os.path.join(LIB_DIR, "libattnio_poison.so")
 SOURCES = ["attnio_api.hip", "tile_model.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip",
-           "attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_unfused_bf16.hip", "stream_rows.hip",
+           "attn_bwd_bf16.hip", "attn_bwd_dq_bf16.hip", "attn_bwd_dkdv_pp_bf16.hip",
+           "attn_unfused_bf16.hip", "stream_rows.hip",
            "attn_fwd_fp8.hip"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit; hipcc -O3

@@ -65,6 +65,17 @@ constexpr int kBwdBQ = 64;  // query rows per dK/dV pipeline step (32 measured s
 #ifndef ATTNIO_DKDV_DIAG_MASK_D128
 #define ATTNIO_DKDV_DIAG_MASK_D128 0
 #endif
+// 1: the dK/dV stage runs in the two-group ping-pong form
+// (attn_bwd_dkdv_pp_bf16.hip) instead of the one-wave form below
+#ifndef ATTNIO_DKDV_PINGPONG_D64
+#define ATTNIO_DKDV_PINGPONG_D64 1
+#endif
+#ifndef ATTNIO_DKDV_PINGPONG_D128
+#define ATTNIO_DKDV_PINGPONG_D128 1
+#endif
+constexpr bool dkdv_pingpong(int d) {
+  return d == 64 ? ATTNIO_DKDV_PINGPONG_D64 != 0 : ATTNIO_DKDV_PINGPONG_D128 != 0;
+}
 constexpr int dkdv_stages(int d) { return d == 64 ? ATTNIO_DKDV_STAGES_D64 : ATTNIO_DKDV_STAGES_D128; }
 constexpr bool dkdv_diag_mask(int d) {
   return d == 64 ? ATTNIO_DKDV_DIAG_MASK_D64 != 0 : ATTNIO_DKDV_DIAG_MASK_D128 != 0;
@@ -410,6 +421,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, ws_d, ws_l, a.N, NP, rows_p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dkdv_pingpong(D)) {
+    e = launch_bwd_dkdv_pp_bf16(a, ws_d, NP, c, stream);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq_bf16(a, ws_d, ws_l, NP, c, stream);
+  }
   constexpr int kv_lds = KvCfg<D, kBwdBQ>::LDS;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, kBwdBQ>), dim3((unsigned)g_kv), dim3(256), kv_lds,
                      stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,

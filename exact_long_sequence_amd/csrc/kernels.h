@@ -114,6 +114,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 // c = scale * log2(e)).
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, const float* ws_d, const float* ws_l, int NP,
                               float c, hipStream_t stream);
+// dK/dV stage in the two-group (ping-pong) form (attn_bwd_dkdv_pp_bf16.hip);
+// same statistics layout and arguments as the dQ stage.
+hipError_t launch_bwd_dkdv_pp_bf16(const BwdArgs& a, const float* ws_d, int NP, float c,
+                                   hipStream_t stream);
 hipError_t launch_fwd_bf16(int variant, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 

@@ -134,3 +134,65 @@ def test_model_detects_a_missing_wait():
     ev = [(b, t, k, a, (z + 1 if (k == "w" and b[0] == "K" and t >= 2) else z))
           for (b, t, k, a, z) in pingpong_events(5)]
     assert check(ev)
+
+
+# ---------------------------------------------------------------------------
+# The two-group dK/dV backward kernel: 32-row blocks of Q, dO and their row
+# statistics in a five-buffer ring (block X in buffer X % 5); group 0 takes
+# the even blocks, group 1 the odd ones.  Block X is read in half step X+1
+# (S, dP by rows, its group's MFMA phase), X+2 (its statistics, the group's
+# VALU phase) and X+3 (dV, dK by transpose reads, the group's next MFMA
+# phase).  In half step h the group on the VALU issues the DMA of block h+1
+# and waits for it at the end of half step h+1; the prologue loads blocks 0
+# and 1 before barrier 0, and group 1 issues block 2 in half step 1.
+
+def dkdv_events(nqb, nbuf=5, issue_lead=1):
+    buf = lambda x: ("QdO", x % nbuf)  # noqa: E731
+    ev = []
+    for x in range(min(2, nqb)):
+        ev.append((buf(x), x, "w", -1, 0))
+    for x in range(2, nqb):
+        h = x - issue_lead  # issued at the start of half step x - 1
+        ev.append((buf(x), x, "w", h, x))
+    for x in range(nqb):
+        for h in (x + 1, x + 2, x + 3):
+            ev.append((buf(x), x, "r", h, h))
+    return ev
+
+
+def dkdv_barriers(nqb, grp):
+    """Workgroup barriers one wave of group grp passes in the kernel (the
+    prologue, two per step, the count-evening barriers, the final one)."""
+    ng = nqb // 2 if grp else (nqb + 1) // 2
+    n = 1 + (1 if grp else 0) + 2 * ng
+    n += 1 if (nqb % 2 == 0) == (grp == 0) else 0
+    return n + 1
+
+
+@pytest.mark.parametrize("nqb", [1, 2, 3, 4, 5, 6, 7, 11, 64])
+def test_dkdv_ring_keeps_the_invariant(nqb):
+    assert check(dkdv_events(nqb)) == []
+
+
+def test_dkdv_ring_of_four_races():
+    """With four buffers block X+4 would land in block X's buffer while its
+    transpose reads (half step X+3) may still run."""
+    bad = check(dkdv_events(9, nbuf=4))
+    assert bad and all("while tile" in b for b in bad), bad
+
+
+@pytest.mark.parametrize("nqb", range(1, 40))
+def test_dkdv_groups_pass_the_same_barriers(nqb):
+    assert dkdv_barriers(nqb, 0) == dkdv_barriers(nqb, 1)
+
+
+def test_dkdv_half_step_of_each_phase():
+    """Group g's MFMA phase of its block X falls in half step X+1 and its VALU
+    phase in X+2: group 0 starts right after barrier 0, group 1 after its
+    extra barrier 1, and every step is two half steps."""
+    for grp in (0, 1):
+        start = 1 + grp  # barriers passed before the first MFMA phase
+        for j in range(6):
+            x = 2 * j + grp
+            assert start + 2 * j == x + 1       # MFMA phase
+            assert start + 2 * j + 1 == x + 2   # VALU phase
