@@ -102,7 +102,8 @@ __device__ __forceinline__ void dma_rows8(const uint8_t* gsrc, int r0, int last_
     const int lch = pch ^ swz8<RB>(row);
     int grow = r0 + row;
     grow = grow < last_ok ? grow : last_ok;
-    const uint32_t o = (uint32_t)(grow * RB + lch * 16);
+    // unsigned: a head's rows span fewer than 2^32 bytes
+    const uint32_t o = (uint32_t)grow * (uint32_t)RB + (uint32_t)(lch * 16);
     const uint32_t l = __builtin_amdgcn_readfirstlane(lds_tile + (uint32_t)((i * THREADS + wave * 64) * 16));
     dma16(gsrc, o, l);
   }
@@ -161,6 +162,11 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
       const i32x4* p = (const i32x4*)(Q + slice + (size_t)qr * RB + ks * 64 + half * 32);
       const i32x4 lo = p[0], hi = p[1];
       qf[ks] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      // wait for Q here: otherwise the compiler's wait for these loads lands
+      // inside the loop, where the hardware counter also holds the K/V DMAs
+      // just issued for the next tile, and every tile waits for its prefetch
+      // (16-byte operands: a 32-byte "v" operand is invalid in the host pass)
+      asm volatile("" ::"v"(lo), "v"(hi));
     }
   }
 
@@ -188,32 +194,60 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
       dma_rows8<RB, BN, THREADS>(Ks, t * BN, kend - 1, st, wave, lane);
       dma_rows8<RB, BN, THREADS>(Vs, t * BN, kend - 1, st + KT, wave, lane);
     };
+    // Per-lane LDS byte offsets of the operand reads within a tile.  A row's
+    // swizzle depends on (row / 2) mod 8 only, so whole 32-row blocks go into
+    // the instruction's offset: V^T transpose read u of d block db at
+    // tro[db][u % 2] + (2 ps + u / 2) * 32 rows (lane 16g + 2e + q supplies key
+    // (2 ps + u/2)*32 + (2 (u%2) + e/4)*8 + 4 (g/2) + e%4, bytes 32 db +
+    // 16 (g%2) + 8 q .. + 7; lane 16g + i receives byte i of those 8 keys,
+    // i.e. bytes t = 8u + e of its operand); K row read of k step ks (low or
+    // high 16 bytes of the lane's 32) at kro[ks][hi] + kb * 32 rows.
+    uint32_t tro[D / 32][2], kro[D / 64][2];
+    {
+      const int g = lane / 16, h = g / 2, e = (lane % 16) / 2, q = lane % 2;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+          const int key = (2 * u2 + e / 4) * 8 + 4 * h + e % 4;
+          const int ch = 2 * db + (g % 2);
+          tro[db][u2] = (uint32_t)(key * RB + ((ch ^ swz8<RB>(key)) * 16) + q * 8);
+        }
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const int ch = ks * 4 + half * 2 + hi;
+          kro[ks][hi] = (uint32_t)(col * RB + ((ch ^ swz8<RB>(col)) * 16));
+        }
+    }
     issue(0);
     wait_dma();
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
+      // opaque copies: the offsets are not expanded into one register per read
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) asm volatile("" : "+v"(tro[db][0]), "+v"(tro[db][1]));
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks) asm volatile("" : "+v"(kro[ks][0]), "+v"(kro[ks][1]));
       if (t + 1 < ntiles) issue(t + 1);
       const char LDS_AS* kt_l = smem + (t & 1) * 2 * KT;
       const char LDS_AS* vt_l = kt_l + KT;
       const int j0 = t * BN;
 
-      // S^T = K Q^T: lane (h, c) holds keys (r/4)*8 + 4h + r%4 of block kb, query c
+      // S^T = K Q^T: lane (h, c) holds keys (r/4)*8 + 4h + r%4 of block kb,
+      // query c; each chain starts from the MFMA's zero accumulator input
       f32x16 s[BN / 32];
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
+      for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const int row = kb * 32 + col;
-#pragma unroll
-        for (int ks = 0; ks < D / 64; ++ks) {
-          const int ch = ks * 4 + half * 2;
-          const char LDS_AS* rp = kt_l + row * RB;
-          const i32x4 lo = *(const i32x4 LDS_AS*)(rp + ((ch ^ swz8<RB>(row)) * 16));
-          const i32x4 hi = *(const i32x4 LDS_AS*)(rp + (((ch + 1) ^ swz8<RB>(row)) * 16));
+        for (int kb = 0; kb < BN / 32; ++kb) {
+          const i32x4 lo = *(const i32x4 LDS_AS*)(kt_l + kro[ks][0] + kb * 32 * RB);
+          const i32x4 hi = *(const i32x4 LDS_AS*)(kt_l + kro[ks][1] + kb * 32 * RB);
           const i32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          s[kb] = mfma_fp8(a, qf[ks], s[kb]);
+          const f32x16 zero = {};
+          s[kb] = mfma_fp8(a, qf[ks], ks == 0 ? zero : s[kb]);
         }
-      }
       // mask (one uniform test per tile, not per score) only the tiles on the
       // diagonal or past kv_len.  Scores stay unscaled: a masked score becomes
       // the infinity that maps to -inf under the scale c (never 0: the launcher
@@ -293,7 +327,6 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
       // (h = g/2), bytes 32 db + 16 (g%2) + 8 q .. + 7; lane 16g + i receives
       // byte i of those 8 keys, i.e. bytes t = 8u + e of its operand.
       {
-        const int g = lane / 16, h = g / 2, e = (lane % 16) / 2, q = lane % 2;
 #pragma unroll
         for (int ps = 0; ps < BN / 64; ++ps)
 #pragma unroll
@@ -301,9 +334,7 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
             i32x8 a;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const int key = (2 * ps + u / 2) * 32 + (2 * (u % 2) + e / 4) * 8 + 4 * h + e % 4;
-              const int ch = 2 * db + (g % 2);
-              const char LDS_AS* ap = vt_l + key * RB + ((ch ^ swz8<RB>(key)) * 16) + q * 8;
+              const char LDS_AS* ap = vt_l + tro[db][u % 2] + (2 * ps + u / 2) * 32 * RB;
               const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)ap);
               a[2 * u] = v2[0];
               a[2 * u + 1] = v2[1];
@@ -338,11 +369,11 @@ void attn_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restric
 
 template <int D, bool CAUSAL>
 hipError_t launch_fp8_t(const Fp8Args& a, hipStream_t stream) {
+  float c = a.scale * a.q_descale * a.k_descale * kLog2e;
+  if (c == 0.f) c = FLT_MIN;  // keeps masked scores at -inf (inf * 0 would be NaN)
   const int n_qtiles = (a.N + 127) / 128;
   const long long grid = (long long)a.B * a.H * n_qtiles;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  float c = a.scale * a.q_descale * a.k_descale * kLog2e;
-  if (c == 0.f) c = FLT_MIN;  // keeps masked scores at -inf (inf * 0 would be NaN)
   constexpr int lds = 2 * 2 * 128 * D;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, (__bf16*)a.o,
