@@ -310,6 +310,86 @@ __device__ __forceinline__ void mfma_stream(const char LDS_AS* vl, const bf16x8 
   }
 }
 
+// The MFMA phase of the split form (two query blocks per wave, ping-pong, row
+// sums on the matrix core): S^T(t) of both blocks first (each K operand read
+// feeds two MFMAs), then the row-sum MFMAs of P(t-1) for both blocks, then
+// the P x V MFMAs of tile t-1 with valu(mp) called after the two MFMAs of V
+// operand mp.  The MFMA wave runs its block-0 softmax of tile t there: VALU
+// work between a wave's own MFMAs runs under them, while the same work in the
+// softmax wave of the SIMD would lengthen the half step.  Operand addressing
+// and read-ahead as in mfma_stream.
+template <class C, int D, int BN, int R, class VALU>
+__device__ __forceinline__ void mfma_stream_split(const char LDS_AS* vl, const bf16x8 (&pb)[2][BN / 16],
+                                                  f32x16 (&acc)[2][D / 32], const bf16x8& sel,
+                                                  f32x4 (&lsum)[2], const char LDS_AS* kl,
+                                                  const bf16x8 (&qf)[2][D / 16], f32x16 (&s)[2][BN / 32],
+                                                  int lane, VALU&& valu) {
+  const int half = lane / 32, col = lane % 32;
+  const int g = lane / 16;
+  const int jr = (lane % 16) / 4;
+  const int qq = lane % 4;
+  constexpr int NQK = (D / 16) * (BN / 32);
+  constexpr int NPV = (BN / 16) * (D / 32);
+  constexpr int NM = NQK + NPV;
+  uint32_t kbase =
+      (uint32_t)(uintptr_t)kl + (uint32_t)(col * C::ROW_BYTES + ((half ^ swz_k<C>(col)) * 16));
+  const int vrow = half * 4 + jr;
+  uint32_t vbase = (uint32_t)(uintptr_t)vl +
+                   (uint32_t)(vrow * C::ROW_BYTES + ((((g % 2) * 2 + qq / 2) ^ swz_v<C>(vrow)) * 16) +
+                              (qq % 2) * 8);
+  asm volatile("" : "+v"(kbase), "+v"(vbase));
+  auto read = [&](int m) __attribute__((always_inline)) {
+    bf16x8 a;
+    if (m < NQK) {
+      const int ks = m / (BN / 32), kb = m % (BN / 32);
+      const uint32_t addr = (kbase ^ (uint32_t)(ks * 32)) + (uint32_t)(kb * 32 * C::ROW_BYTES);
+      a = *(const bf16x8 LDS_AS*)(uintptr_t)addr;
+    } else {
+      const int mp = m - NQK, st = mp / (D / 32), db = mp % (D / 32);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t addr = (vbase ^ (uint32_t)(db * 64)) + (uint32_t)((st * 16 + u * 8) * C::ROW_BYTES);
+        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(uintptr_t)addr);
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
+      }
+    }
+    return a;
+  };
+  bf16x8 ring[R + 1];
+#pragma unroll
+  for (int m = 0; m < R && m < NM; ++m) ring[m] = read(m);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m + R < NM) ring[(m + R) % (R + 1)] = read(m + R);
+    const bf16x8 a = ring[m % (R + 1)];
+    if (m < NQK) {
+      const int ks = m / (BN / 32), kb = m % (BN / 32);
+      const f32x16 zero = {};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], ks == 0 ? zero : s[qb][kb], 0, 0, 0);
+      if (m == NQK - 1) {
+        const f32x4 zero4 = {};
+#pragma unroll
+        for (int st = 0; st < BN / 16; ++st)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb[qb][st], st == 0 ? zero4 : lsum[qb],
+                                                               0, 0, 0);
+      }
+    } else {
+      const int mp = m - NQK, st = mp / (D / 32), db = mp % (D / 32);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb][st], acc[qb][db], 0, 0, 0);
+      valu(mp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Masked scores become -inf (or +inf when the scale is negative, so that they
 // still map to exp2(-inf) = 0).  Only diagonal and padding tiles call this.
 template <int BN, bool CAUSAL, bool NEG>
@@ -386,9 +466,13 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // workgroups resident per CU (the residency the register budget and the
 // causal key order assume), causal key snake, row sums on the matrix core.
 template <int D_, int BN_, int WAVES_, int QB_, int STAGES_, bool PINGPONG_, int WG_PER_CU_, bool SNAKE_,
-          bool RS_MFMA_, bool RS_IN_STREAM_ = false>
+          bool RS_MFMA_, bool RS_IN_STREAM_ = false, bool SPLIT_ = false>
 struct Variant {
   static constexpr int D = D_, BN = BN_, WAVES = WAVES_, QB = QB_;
+  // split softmax: with two query blocks per wave in the ping-pong form, the
+  // MFMA wave computes its block-0 softmax inside its own MFMA phase (see
+  // mfma_stream_split) and the softmax half step keeps block 1
+  static constexpr bool SPLIT = SPLIT_ && PINGPONG_ && QB_ == 2 && RS_MFMA_ && RS_IN_STREAM_;
   static constexpr int STAGES = PINGPONG_ ? 2 : STAGES_;
   static constexpr bool PINGPONG = PINGPONG_, KEYS_SNAKE = SNAKE_, RS_MFMA = RS_MFMA_;
   // where the matrix-core row sums are issued in the ping-pong form: by the
@@ -619,23 +703,24 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   // accumulator may already hold an overflowed product, and the workgroup then
   // recomputes its rows with the shift checked before every tile (the safe
   // pass below).
+  auto fold_one = [&](int qb) __attribute__((always_inline)) {
+    const float rs = lsum[qb][0];
+    bad = bad || !(rs <= kSafeSumMax);
+    l_run[qb] += rs;
+    if (rs > kLazySumMax && rs <= kSafeSumMax) {
+      const float mv = floorf(__builtin_amdgcn_logf(rs));
+      const float alpha = __builtin_amdgcn_exp2f(-mv);
+      m_run[qb] += mv;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      l_run[qb] *= alpha;
+    }
+  };
   auto fold_sum = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float rs = lsum[qb][0];
-      bad = bad || !(rs <= kSafeSumMax);
-      l_run[qb] += rs;
-      if (rs > kLazySumMax && rs <= kSafeSumMax) {
-        const float mv = floorf(__builtin_amdgcn_logf(rs));
-        const float alpha = __builtin_amdgcn_exp2f(-mv);
-        m_run[qb] += mv;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-        l_run[qb] *= alpha;
-      }
-    }
+    for (int qb = 0; qb < QB; ++qb) fold_one(qb);
   };
   // VALU part of tile t: fold the previous tile's row sums, mask, shift (first
   // visible tile, or every tile in the safe pass), P(t).
@@ -663,6 +748,56 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         l_run[qb] += lt;
       }
     }
+  };
+
+  // Split form, block 0 inside the MFMA phase of tile t: the fold of tile
+  // t-1's row sums and the shift decisions of tile t, as in fold_one and
+  // update_shift, except that acc[0] is still accumulating P(t-1) V(t-1)
+  // there, so its rescale is recorded (a0, r0) and applied after the phase;
+  // l and the shift change at once.
+  auto split_head0 = [&](int t, auto safe_tag, float& a0, bool& r0) __attribute__((always_inline)) {
+    constexpr bool SAFE = decltype(safe_tag)::value;
+    const float rs = lsum[0][0];
+    bad = bad || !(rs <= kSafeSumMax);
+    l_run[0] += rs;
+    if (rs > kLazySumMax && rs <= kSafeSumMax) {
+      const float mv = floorf(__builtin_amdgcn_logf(rs));
+      const float alpha = __builtin_amdgcn_exp2f(-mv);
+      m_run[0] += mv;
+      l_run[0] *= alpha;
+      a0 *= alpha;
+      r0 = true;
+    }
+    if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0[0], ktile(t) * BN, L, qw0 + col, half);
+    if (SAFE || m_run[0] == -INFINITY) {
+      const float m_tile = row_extreme<BN, NEG_SCALE>(s0[0]) * c;
+      if (m_tile > m_run[0] + kTauLog2) {
+        const float m_new = fmaxf(m_run[0], m_tile);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[0] - m_new);
+        m_run[0] = m_new;
+        l_run[0] *= alpha;
+        a0 *= alpha;
+        r0 = true;
+      }
+    }
+  };
+  // P operand i of block 0 (keys 16 i .. 16 i + 15), as softmax_p packs it
+  auto split_pack0 = [&](int i, bf16x8 (&pbn)[BN / 16]) __attribute__((always_inline)) {
+    const float m0 = m_run[0] == -INFINITY ? 0.f : m_run[0];
+    const int kb = i / 2, sp = i % 2;
+    bf16x8 p;
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8)
+      p[t8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[0][kb][sp * 8 + t8], c, -m0));
+    pbn[i] = p;
+  };
+  // the softmax half step of the split form: block 1 only
+  auto softmax_block1 = [&](int t, auto safe_tag) __attribute__((always_inline)) {
+    constexpr bool SAFE = decltype(safe_tag)::value;
+    fold_one(1);
+    if (need_mask(t)) mask_tile<BN, CAUSAL, NEG_SCALE>(s0[1], ktile(t) * BN, L, qw0 + 32 + col, half);
+    if (SAFE || m_run[1] == -INFINITY) update_shift(1);
+    softmax_p<BN, false>(s0[1], c, m_run[1] == -INFINITY ? 0.f : m_run[1], pb[1]);
   };
 
   // One pass over the keys.  The safe pass is a second, straight-line copy
@@ -710,7 +845,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       if (t + 1 < ntiles) issue(half_tag, WAVES / 2, Kg, false, t + 1, kd(t + 1));
     };
     // one half-step pair of tile t; `mf` is the MFMA phase
-    auto step = [&](int t, auto st_tag, auto&& mf) __attribute__((always_inline)) {
+    auto step = [&](int t, auto&& mf, auto&& vf) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(2);
       mf();
       __builtin_amdgcn_s_setprio(0);
@@ -727,7 +862,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       }
       if (grp == 1) issue_step(t + 1);
       else issue(half_tag, 0, Vg, true, t, vd(t));
-      softmax_tile(t, st_tag);
+      vf();
       // keep the softmax in this half step: without these uses the compiler
       // sinks the exponentials past the barrier, next to the P x V MFMAs
 #pragma unroll
@@ -750,14 +885,39 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         issue_step(0);
         __syncthreads();
       }
-      step(0, safe_tag, [&]() __attribute__((always_inline)) {
+      step(0, [&]() __attribute__((always_inline)) {
         mfma_stream<C, D, BN, QB, R, false, true, false>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
-      });
-      for (int t = 1; t < ntiles; ++t)
-        step(t, safe_tag, [&]() __attribute__((always_inline)) {
-          mfma_stream<C, D, BN, QB, R, true, true, RS_STREAM>(smem + vd(t - 1), pb, acc, sel, lsum,
-                                                              smem + kd(t), qf, s0, lane);
-        });
+      }, [&]() __attribute__((always_inline)) { softmax_tile(0, safe_tag); });
+      if constexpr (VT::SPLIT) {
+        // the P x V operands of block 0: P(t-1) in pb[0] (read by this
+        // phase's MFMAs), P(t) built in pbn and moved to pb[0] after them
+        bf16x8 pbn[BN / 16];
+        constexpr int NPV = (BN / 16) * (D / 32), KP = NPV / (BN / 16);
+        for (int t = 1; t < ntiles; ++t)
+          step(t, [&]() __attribute__((always_inline)) {
+            float a0 = 1.f;
+            bool r0 = false;
+            mfma_stream_split<C, D, BN, R>(smem + vd(t - 1), pb, acc, sel, lsum, smem + kd(t), qf, s0, lane,
+                                           [&](int mp) __attribute__((always_inline)) {
+                                             if (mp == 0) split_head0(t, safe_tag, a0, r0);
+                                             if (mp % KP == KP - 1) split_pack0(mp / KP, pbn);
+                                           });
+            if (r0) {
+#pragma unroll
+              for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[0][db][r] *= a0;
+            }
+#pragma unroll
+            for (int i = 0; i < BN / 16; ++i) pb[0][i] = pbn[i];
+          }, [&]() __attribute__((always_inline)) { softmax_block1(t, safe_tag); });
+      } else {
+        for (int t = 1; t < ntiles; ++t)
+          step(t, [&]() __attribute__((always_inline)) {
+            mfma_stream<C, D, BN, QB, R, true, true, RS_STREAM>(smem + vd(t - 1), pb, acc, sel, lsum,
+                                                                smem + kd(t), qf, s0, lane);
+          }, [&]() __attribute__((always_inline)) { softmax_tile(t, safe_tag); });
+      }
       __builtin_amdgcn_s_setprio(2);
       mfma_stream<C, D, BN, QB, R, true, false, RS_STREAM>(smem + vd(ntiles - 1), pb, acc, sel, lsum, smem,
                                                            qf, s0, lane);
@@ -917,7 +1077,10 @@ using V64_PP64_QB2 = Variant<64, 64, 8, 2, 2, true, 1, true, true>;
 using V64_PP64 = Variant<64, 64, 8, 1, 2, true, 2, true, false>;
 using V64_PP128 = Variant<64, 128, 8, 1, 2, true, 1, true, true>;
 using V64_PP64_W16 = Variant<64, 64, 16, 1, 2, true, 1, true, false>;
-using V64_PP64_QB2_RSS = Variant<64, 64, 8, 2, 2, true, 1, true, true, true>;
+#ifndef ATTNIO_FWD_SPLIT_D64
+#define ATTNIO_FWD_SPLIT_D64 1
+#endif
+using V64_PP64_QB2_RSS = Variant<64, 64, 8, 2, 2, true, 1, true, true, true, ATTNIO_FWD_SPLIT_D64 != 0>;
 using V128_PP128_RSS = Variant<128, 128, 8, 1, 2, true, 1, true, true, true>;
 
 template <class VT>
