@@ -888,9 +888,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
       step(0, [&]() __attribute__((always_inline)) {
         mfma_stream<C, D, BN, QB, R, false, true, false>(smem, pb, acc, sel, lsum, smem + kd(0), qf, s0, lane);
       }, [&]() __attribute__((always_inline)) { softmax_tile(0, safe_tag); });
-      if constexpr (VT::SPLIT) {
+      if constexpr (VT::SPLIT && !decltype(safe_tag)::value) {
         // the P x V operands of block 0: P(t-1) in pb[0] (read by this
-        // phase's MFMAs), P(t) built in pbn and moved to pb[0] after them
+        // phase's MFMAs), P(t) built in pbn and moved to pb[0] after them.
+        // (The safe pass, rare, takes the plain form below: the split form's
+        // extra live values there pushed the kernel past the register file.)
         bf16x8 pbn[BN / 16];
         constexpr int NPV = (BN / 16) * (D / 32), KP = NPV / (BN / 16);
         for (int t = 1; t < ntiles; ++t)
