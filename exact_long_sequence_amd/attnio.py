@@ -108,7 +108,7 @@ _DTYPES = {"bf16": 0, "f32": 1, "fp8": 2}
 class AttnTiling(ctypes.Structure):
     """attn_tiling of include/attnio.h."""
     _fields_ = [(n, ctypes.c_int) for n in ("d", "BM", "BN", "stages", "waves", "lds_bytes", "wg_per_cu",
-                                            "qb", "pingpong", "rowsum_mfma", "rowsum_in_stream")]
+                                            "qb", "pingpong", "rowsum_mfma", "rowsum_in_stream", "mfma16")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -466,9 +466,11 @@ __device__ __forceinline__ float softmax_p(const f32x16 (&s)[BN / 32], float c, 
 // workgroups resident per CU (the residency the register budget and the
 // causal key order assume), causal key snake, row sums on the matrix core.
 template <int D_, int BN_, int WAVES_, int QB_, int STAGES_, bool PINGPONG_, int WG_PER_CU_, bool SNAKE_,
-          bool RS_MFMA_, bool RS_IN_STREAM_ = false, bool SPLIT_ = false>
+          bool RS_MFMA_, bool RS_IN_STREAM_ = false, bool SPLIT_ = false, bool MF16_ = false>
 struct Variant {
   static constexpr int D = D_, BN = BN_, WAVES = WAVES_, QB = QB_;
+  // every product on the 16x16x32 MFMA (attn_fwd_bf16_mf16_kernel below)
+  static constexpr bool MF16 = MF16_;
   // split softmax: with two query blocks per wave in the ping-pong form, the
   // MFMA wave computes its block-0 softmax inside its own MFMA phase (see
   // mfma_stream_split) and the softmax half step keeps block 1
@@ -1032,6 +1034,454 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
   }
 }
 
+// ----------------------------------------------------------------------------
+// The 16x16x32 form of the ping-pong kernel (d = 128).
+// ----------------------------------------------------------------------------
+// Same schedule, tiles, LDS ring, hand-over and lazy shift as the kernel
+// above, with every product on v_mfma_f32_16x16x32_bf16.  On MI355X a long
+// all-CU MFMA stream on random operands is power limited, and the smaller
+// shape, which reads and writes half the accumulator data per multiply-add,
+// delivered 0.83 of the bf16 nameplate against 0.70 for 32x32x16 (measured).
+//
+// A wave's 32 queries form two blocks of 16 (h = 0, 1); lane l = 16 g + n
+// owns query n of each block.  Per 16-key block kb, S^T (16 keys x 16
+// queries) has lane (g, n) holding keys 16 kb + 4g .. +3 of query n.  P^T of
+// a 32-key step st (the B operand of P x V: 32 keys x 16 queries) takes, in
+// lane (g, n), the keys 32 st + 16 u + 4 g + e of blocks 2 st + u (u = 0, 1,
+// e = 0..3) as reduction index k = 8 g + 4 u + e: built lane-locally from
+// two S^T blocks.  The V operand (A: 16 d-rows x 32 keys) is read in the same
+// key order by two transpose reads of four key rows.  O^T (16 d x 16 queries
+// per block) has lane (g, n) holding d = 16 db + 4 g .. +3 of query n.  Row
+// sums: an all-ones A operand times P^T gives every output row the column
+// sums, so each lane receives its own query's sum over the step.  Row maxima
+// (first visible tile, safe pass) reduce over the four lanes n, n + 16,
+// n + 32, n + 48 of a query (two lane swaps).
+
+// Chunk swizzle of V rows for the transpose reads of this form: the four
+// rows of one read and the two 16-lane groups of a half-wave (rows 4 apart)
+// land on distinct 16-byte chunks, 512 bytes over all banks.  Period 8 rows.
+template <class C>
+__device__ __forceinline__ int swz_v16(int row) {
+  static_assert(C::CHUNKS == 16, "d = 128 rows");
+  return 2 * ((row % 4) + 4 * ((row / 4) % 2));
+}
+
+// v_permlane16_swap with both operands = x: the pair is {own, lane ^ 16}.
+__device__ __forceinline__ u32x2 swap_rows16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u32x2 out = {r[0], r[1]};
+  return out;
+}
+
+// One MFMA phase (as mfma_stream): DO_PV, O^T += V^T P^T over the tile's
+// (BN/32) x (D/16) V operands (and, with DO_RS, the row sums of each 32-key
+// step); DO_QK, S^T = K Q^T over (D/32) x (BN/16) K operands.  Each operand
+// feeds two MFMAs (query blocks h = 0, 1).  Operand addresses as in
+// mfma_stream: a lane base XOR a compile-time constant plus an immediate
+// row offset:
+//   K: row 16 kb + n, chunk (4 ks + g) ^ n = (kbase ^ 64 ks) + 16 kb rows,
+//   V: row 32 st + 16 u + 4 g + j, chunk (2 db + q / 2) ^ swz_v16
+//      = (vbase ^ 32 db) + (32 st + 16 u) rows   (lane n = 4 j + q).
+template <class C, int D, int BN, int R, bool DO_PV, bool DO_QK, bool DO_RS>
+__device__ __forceinline__ void mfma_stream16(const char LDS_AS* vl, const bf16x8 (&pb)[2][BN / 32],
+                                              f32x4 (&acc)[2][D / 16], const bf16x8& ones, f32x4 (&lsum)[2],
+                                              const char LDS_AS* kl, const bf16x8 (&qf)[2][D / 32],
+                                              f32x4 (&s)[2][BN / 16], int lane) {
+  const int g = lane / 16, n = lane % 16;
+  const int j = n / 4, q = n % 4;
+  constexpr int NPV = DO_PV ? (BN / 32) * (D / 16) : 0;
+  constexpr int NQK = DO_QK ? (D / 32) * (BN / 16) : 0;
+  constexpr int NM = NPV + NQK;
+  static_assert(D == 128 && C::ROWS_PER_256 == 1, "16x16x32 form: d = 128");
+  uint32_t kbase = (uint32_t)(uintptr_t)kl + (uint32_t)(n * C::ROW_BYTES + ((g ^ swz_k<C>(n)) * 16));
+  const int vrow = 4 * g + j;
+  uint32_t vbase = (uint32_t)(uintptr_t)vl +
+                   (uint32_t)(vrow * C::ROW_BYTES + (((q / 2) ^ swz_v16<C>(vrow)) * 16) + (q % 2) * 8);
+  asm volatile("" : "+v"(kbase), "+v"(vbase));
+  auto read = [&](int m) __attribute__((always_inline)) {
+    bf16x8 a;
+    if (m < NPV) {
+      const int st = m / (D / 16), db = m % (D / 16);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t addr = (vbase ^ (uint32_t)(db * 32)) + (uint32_t)((st * 32 + u * 16) * C::ROW_BYTES);
+        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(uintptr_t)addr);
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, v4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[u * 4 + e] = vb[e];
+      }
+    } else {
+      const int mq = m - NPV;
+      const int ks = mq / (BN / 16), kb = mq % (BN / 16);
+      const uint32_t addr = (kbase ^ (uint32_t)(ks * 64)) + (uint32_t)(kb * 16 * C::ROW_BYTES);
+      a = *(const bf16x8 LDS_AS*)(uintptr_t)addr;
+    }
+    return a;
+  };
+  bf16x8 ring[R + 1];
+#pragma unroll
+  for (int m = 0; m < R && m < NM; ++m) ring[m] = read(m);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m + R < NM) ring[(m + R) % (R + 1)] = read(m + R);
+    const bf16x8 a = ring[m % (R + 1)];
+    const f32x4 zero4 = {};
+    if (m < NPV) {
+      const int st = m / (D / 16), db = m % (D / 16);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[h][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[h][st], acc[h][db], 0, 0, 0);
+      if (DO_RS && db == D / 16 - 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          lsum[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[h][st], st == 0 ? zero4 : lsum[h], 0, 0, 0);
+      }
+    } else {
+      const int mq = m - NPV;
+      const int ks = mq / (BN / 16), kb = mq % (BN / 16);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        s[h][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[h][ks], ks == 0 ? zero4 : s[h][kb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <class VT, bool CAUSAL, bool NEG_SCALE>
+__global__ __launch_bounds__(64 * VT::WAVES, (VT::WAVES / 4) * VT::WG_PER_CU)
+void attn_fwd_bf16_mf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                               const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                               const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H, int N,
+                               float c, int n_qtiles) {
+  constexpr int D = VT::D, BN = VT::BN, WAVES = VT::WAVES, WG_PER_CU = VT::WG_PER_CU;
+  constexpr bool KEYS_SNAKE = VT::KEYS_SNAKE;
+  constexpr int R = read_ahead<1>();  // each operand read feeds two 16-cycle MFMAs
+  using C = typename VT::C;
+  static_assert(VT::PINGPONG && VT::QB == 1 && VT::RS_MFMA && WAVES % 2 == 0, "16x16x32 form: ping-pong, 32 queries per wave");
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int g = lane / 16;  // key (S^T) or d (O^T) group of the lane
+  const int n = lane % 16;  // the query of each 16-query block this lane owns
+
+  // ---- work assignment, key order: as in attn_fwd_bf16_kernel ----
+  const int G = gridDim.x;
+  const int x = blockIdx.x;
+  const int xcd = x % 8, idx = x / 8;
+  int bh, qt;
+  if ((G / n_qtiles) % 8 == 0) {
+    bh = xcd + 8 * (idx / n_qtiles);
+    qt = idx % n_qtiles;
+  } else {
+    const int per = G / 8, rem = G % 8;
+    const int logical = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    bh = logical / n_qtiles;
+    qt = logical % n_qtiles;
+  }
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int b = bh / H;
+  int L = N;
+  if (kv_len != nullptr) {
+    L = kv_len[b];
+    L = L < 0 ? 0 : (L > N ? N : L);
+  }
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int q0 = qt * C::BM;
+  int kend = L;
+  if (CAUSAL) kend = min(kend, min(N, q0 + C::BM));
+  kend = __builtin_amdgcn_readfirstlane(kend);
+  const int ntiles = (kend + BN - 1) / BN;
+  constexpr int RESIDENT = 32 * WG_PER_CU;
+  const bool keys_down = CAUSAL && KEYS_SNAKE && (((n_qtiles - 1 - qt) / RESIDENT) & 1);
+  auto ktile = [&](int t) __attribute__((always_inline)) { return keys_down ? ntiles - 1 - t : t; };
+
+  const size_t slice = (size_t)bh * N * D;
+  const __bf16* Qs = Q + slice;
+  const char* Kg = (const char*)(K + slice);
+  const char* Vg = (const char*)(V + slice);
+  __bf16* Os = O + slice;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+
+  // DMA of a K or V tile by NW waves from W0 (as in attn_fwd_bf16_kernel;
+  // V rows take this form's swizzle)
+  auto issue = [&](auto nw_tag, int w0, const char* gsrc, bool is_v, int t, uint32_t dst)
+      __attribute__((always_inline)) {
+    constexpr int NW = decltype(nw_tag)::value;
+    constexpr int TH = 64 * NW;
+    constexpr int NLOADS = C::TILE_BYTES / 16 / TH;
+    constexpr int RSTEP = TH * 16 / C::ROW_BYTES;
+    static_assert(C::TILE_BYTES % (16 * TH) == 0, "tile must split evenly over the issuing waves");
+    static_assert((TH * 16) % C::ROW_BYTES == 0 && RSTEP % 16 == 0, "loads must step by whole swizzle periods");
+    const int j0 = ktile(t) * BN;
+    const char* gt = gsrc + (size_t)j0 * C::ROW_BYTES;
+    int last = kend - 1 - j0;
+    const int wl = wave - w0;
+    const int pos0 = (wl * 64 + lane) * 16;
+    const int row0 = pos0 / C::ROW_BYTES;
+    const int lch = ((pos0 % C::ROW_BYTES) / 16) ^ (is_v ? swz_v16<C>(row0) : swz_k<C>(row0));
+    const uint32_t l0 = lds_base + dst + (uint32_t)(wl * 64 * 16);
+    if (last >= BN - 1) {
+      uint32_t o = (uint32_t)(row0 * C::ROW_BYTES + lch * 16);
+      asm volatile("" : "+v"(o));
+#pragma unroll
+      for (int i = 0; i < NLOADS; ++i)
+        dma16(gt, o + (uint32_t)(i * TH * 16), __builtin_amdgcn_readfirstlane(l0 + (uint32_t)(i * TH * 16)));
+    } else {
+      last = __builtin_amdgcn_readfirstlane(last);
+      int r0 = row0, c16 = lch * 16;
+      asm volatile("" : "+s"(last), "+v"(r0), "+v"(c16));
+#pragma unroll
+      for (int i = 0; i < NLOADS; ++i) {
+        const int lim = last - i * RSTEP;
+        const int grow = r0 < lim ? r0 : lim;
+        const uint32_t o = (uint32_t)(grow * C::ROW_BYTES + c16) + (uint32_t)(i * TH * 16);
+        dma16(gt, o, __builtin_amdgcn_readfirstlane(l0 + (uint32_t)(i * TH * 16)));
+      }
+    }
+  };
+  const int qw0 = q0 + wave * 32;  // first query row of this wave; block h: qw0 + 16 h + n
+  auto need_mask = [&](int t) __attribute__((always_inline)) {
+    const int j0 = ktile(t) * BN;
+    return (j0 + BN > L) || (CAUSAL && (j0 + BN - 1 > qw0));
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane (g, n) holds
+  //      Q[qw0 + 16 h + n][32 ks + 8 g .. +7] ----
+  bf16x8 qf[2][D / 32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int qrow = qw0 + 16 * h + n;
+    const int qrow_c = qrow < N ? qrow : N - 1;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      qf[h][ks] = __builtin_nontemporal_load((const bf16x8*)(Qs + (size_t)qrow_c * D + ks * 32 + g * 8));
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) asm volatile("" ::"v"(qf[h][ks]));
+
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+
+  constexpr bool RS_STREAM = VT::RS_IN_STREAM;
+  f32x4 acc[2][D / 16];
+  float m_run[2], l_run[2];
+  f32x4 lsum[2];
+  bool bad;
+  f32x4 s0[2][BN / 16];
+  bf16x8 pb[2][BN / 32];
+
+  // row extreme of the raw scores of block h (max, or min for a negative
+  // scale) over the lane's values and the three other lanes of its query
+  auto row_extreme16 = [&](int h) __attribute__((always_inline)) {
+    float m4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m4[r] = s0[h][0][r];
+#pragma unroll
+    for (int kb = 1; kb < BN / 16; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m4[r] = NEG_SCALE ? fminf(m4[r], s0[h][kb][r]) : fmaxf(m4[r], s0[h][kb][r]);
+    float mx = NEG_SCALE ? fminf(fminf(m4[0], m4[1]), fminf(m4[2], m4[3]))
+                         : fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    const u32x2 p32 = swap_halves(mx);
+    mx = NEG_SCALE ? fminf(__uint_as_float(p32[0]), __uint_as_float(p32[1]))
+                   : fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    const u32x2 p16 = swap_rows16(mx);
+    return NEG_SCALE ? fminf(__uint_as_float(p16[0]), __uint_as_float(p16[1]))
+                     : fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  };
+  auto update_shift = [&](int h) __attribute__((always_inline)) {
+    const float m_tile = row_extreme16(h) * c;
+    if (m_tile > m_run[h] + kTauLog2) {
+      const float m_new = fmaxf(m_run[h], m_tile);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[h] - m_new);
+      m_run[h] = m_new;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[h][db][r] *= alpha;
+      l_run[h] *= alpha;
+    }
+  };
+  auto rowsum_mfma = [&]() __attribute__((always_inline)) {
+    const f32x4 zero4 = {};
+#pragma unroll
+    for (int st = 0; st < BN / 32; ++st)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        lsum[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[h][st], st == 0 ? zero4 : lsum[h], 0, 0, 0);
+  };
+  // fold the previous tile's row sums (lazy shift and guard as in the 32x32
+  // form's fold_sum)
+  auto fold_sum = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float rs = lsum[h][0];
+      bad = bad || !(rs <= kSafeSumMax);
+      l_run[h] += rs;
+      if (rs > kLazySumMax && rs <= kSafeSumMax) {
+        const float mv = floorf(__builtin_amdgcn_logf(rs));
+        const float alpha = __builtin_amdgcn_exp2f(-mv);
+        m_run[h] += mv;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[h][db][r] *= alpha;
+        l_run[h] *= alpha;
+      }
+    }
+  };
+  auto softmax_tile = [&](int t, auto safe_tag) __attribute__((always_inline)) {
+    constexpr bool SAFE = decltype(safe_tag)::value;
+    fold_sum();
+    const bool msk = need_mask(t);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (msk) {
+        // element (kb, r) holds key j0 + 16 kb + 4 g + r: visible iff
+        // 16 kb + r <= lim (one per-lane bound per tile, so that no per-element
+        // key offset is kept live across the loop)
+        const int j0 = ktile(t) * BN, qrow = qw0 + 16 * h + n;
+        int lim = L - 1 - j0 - 4 * g;
+        if (CAUSAL) lim = min(lim, qrow - j0 - 4 * g);
+#pragma unroll
+        for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s0[h][kb][r] = (kb * 16 + r <= lim) ? s0[h][kb][r] : (NEG_SCALE ? INFINITY : -INFINITY);
+      }
+      if (SAFE || m_run[h] == -INFINITY) update_shift(h);
+      const float mu = m_run[h] == -INFINITY ? 0.f : m_run[h];
+#pragma unroll
+      for (int st = 0; st < BN / 32; ++st) {
+        bf16x8 p;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[u * 4 + e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s0[h][2 * st + u][e], c, -mu));
+        pb[h][st] = p;
+      }
+    }
+  };
+
+  auto run_pass = [&](auto safe_tag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[h][db][r] = 0.f;
+      m_run[h] = -INFINITY;
+      l_run[h] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lsum[h][r] = 0.f;
+    }
+    bad = false;
+    // ping-pong schedule, ring hand-over and DMA split exactly as in the
+    // 32x32 kernel's ping-pong form
+    const int grp = wave / (WAVES / 2);
+    auto kd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((t & 1) * C::TILE_BYTES); };
+    auto vd = [&](int t) __attribute__((always_inline)) { return (uint32_t)((2 + (t & 1)) * C::TILE_BYTES); };
+    std::integral_constant<int, WAVES / 2> half_tag;
+    std::integral_constant<int, WAVES> all_tag;
+    auto issue_step = [&](int t) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) issue(half_tag, WAVES / 2, Kg, false, t + 1, kd(t + 1));
+    };
+    auto step = [&](int t, auto&& mf) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(2);
+      mf();
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 1) wait_dma();
+      __syncthreads();
+      if (!RS_STREAM && t > 0) rowsum_mfma();
+      if (kPoison && grp == 1) {
+        const int gt = tid - 64 * (WAVES / 2);
+        if (t >= 1) poison_lds(lds_base + vd(t + 1), C::TILE_BYTES, 64 * (WAVES / 2), gt);
+        if (t + 2 < ntiles) poison_lds(lds_base + kd(t + 2), C::TILE_BYTES, 64 * (WAVES / 2), gt);
+      }
+      if (grp == 1) issue_step(t + 1);
+      else issue(half_tag, 0, Vg, true, t, vd(t));
+      softmax_tile(t, safe_tag);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < BN / 32; ++i) asm volatile("" ::"v"(pb[h][i]));
+        asm volatile("" ::"v"(l_run[h]));
+      }
+      if (grp == 0) wait_dma();
+      __syncthreads();
+    };
+    if (ntiles > 0) {
+      if constexpr (C::TILE_BYTES % (16 * C::THREADS) == 0) issue(all_tag, 0, Kg, false, 0, kd(0));
+      else if (grp == 0) issue(half_tag, 0, Kg, false, 0, kd(0));
+      wait_dma();
+      __syncthreads();
+      if (grp == 1) {
+        issue_step(0);
+        __syncthreads();
+      }
+      step(0, [&]() __attribute__((always_inline)) {
+        mfma_stream16<C, D, BN, R, false, true, false>(smem, pb, acc, ones, lsum, smem + kd(0), qf, s0, lane);
+      });
+      for (int t = 1; t < ntiles; ++t)
+        step(t, [&]() __attribute__((always_inline)) {
+          mfma_stream16<C, D, BN, R, true, true, RS_STREAM>(smem + vd(t - 1), pb, acc, ones, lsum, smem + kd(t), qf,
+                                                            s0, lane);
+        });
+      __builtin_amdgcn_s_setprio(2);
+      mfma_stream16<C, D, BN, R, true, false, RS_STREAM>(smem + vd(ntiles - 1), pb, acc, ones, lsum, smem, qf, s0,
+                                                         lane);
+      __builtin_amdgcn_s_setprio(0);
+      if (!RS_STREAM) rowsum_mfma();
+      fold_sum();
+      if (grp == 0) __syncthreads();  // group 1's last softmax barrier
+    }
+  };
+  int LDS_AS* vote = (int LDS_AS*)(smem + C::LDS_ALLOC);
+  if (tid == 0) *vote = 0;
+  run_pass(std::false_type{});
+  if (bad) *vote = 1;
+  __syncthreads();
+  if (*vote != 0) run_pass(std::true_type{});
+
+  // ---------------- epilogue: O = O^T / l (as in attn_fwd_bf16_kernel) ----------------
+  __syncthreads();
+  char LDS_AS* ost = smem + wave * 32 * C::ROW_BYTES;  // this wave's 32 rows: row 16 h + n
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float l_tot = l_run[h];
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int row = 16 * h + n;
+    const int qrow = qw0 + row;
+    if (lse != nullptr && g == 0 && qrow < N)
+      __builtin_nontemporal_store(l_tot > 0.f ? (m_run[h] + log2f(l_tot)) * kLn2 : -INFINITY,
+                                  lse + (size_t)bh * N + qrow);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[h][db][e] * inv);
+      const int byte = (db * 16 + g * 4) * 2;  // within the row
+      const int ch = (byte / 16) ^ (row % C::CHUNKS);
+      *(bf16x4 LDS_AS*)(ost + row * C::ROW_BYTES + ch * 16 + byte % 16) = o;
+    }
+  }
+  constexpr int ROWS_PER_STORE = 64 / C::CHUNKS;
+#pragma unroll
+  for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
+    const int row = i * ROWS_PER_STORE + lane / C::CHUNKS;
+    const int chunk = lane % C::CHUNKS;
+    const u32x4 v = *(const u32x4 LDS_AS*)(ost + row * C::ROW_BYTES + ((chunk ^ (row % C::CHUNKS)) * 16));
+    if (qw0 + row < N) __builtin_nontemporal_store(v, (u32x4*)(Os + (size_t)(qw0 + row) * D + chunk * 8));
+  }
+}
+
 template <class VT, bool CAUSAL, bool NEG>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   using C = typename VT::C;
@@ -1044,10 +1494,17 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   // score maps to exp2(0) = 1 exactly: uniform weights, as for c = 0
   float c = a.scale * kLog2e;
   if (c == 0.f) c = FLT_MIN;
-  auto kern = attn_fwd_bf16_kernel<VT, CAUSAL, NEG>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_ALLOC + 16, stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
-                     a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
+  if constexpr (VT::MF16) {
+    auto kern = attn_fwd_bf16_mf16_kernel<VT, CAUSAL, NEG>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_ALLOC + 16, stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
+                       a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
+  } else {
+    auto kern = attn_fwd_bf16_kernel<VT, CAUSAL, NEG>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), C::LDS_ALLOC + 16, stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o,
+                       a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
+  }
   return hipGetLastError();
 }
 
@@ -1084,12 +1541,13 @@ using V64_PP64_W16 = Variant<64, 64, 16, 1, 2, true, 1, true, false>;
 #endif
 using V64_PP64_QB2_RSS = Variant<64, 64, 8, 2, 2, true, 1, true, true, true, ATTNIO_FWD_SPLIT_D64 != 0>;
 using V128_PP128_RSS = Variant<128, 128, 8, 1, 2, true, 1, true, true, true>;
+using V128_PP128_RSS_M16 = Variant<128, 128, 8, 1, 2, true, 1, true, true, true, false, true>;
 
 template <class VT>
 constexpr Tiling tiling_of() {
   using C = typename VT::C;
   return Tiling{VT::D, C::BM, VT::BN, C::STAGES, VT::WAVES, C::LDS_ALLOC + 16, VT::WG_PER_CU, VT::QB,
-                VT::PINGPONG ? 1 : 0, VT::RS_MFMA ? 1 : 0, VT::RS_IN_STREAM ? 1 : 0};
+                VT::PINGPONG ? 1 : 0, VT::RS_MFMA ? 1 : 0, VT::RS_IN_STREAM ? 1 : 0, VT::MF16 ? 1 : 0};
 }
 
 struct Entry {
@@ -1107,6 +1565,7 @@ const Entry kEntries[] = {
     {tiling_of<V64_PP64_W16>(), &dispatch_mask<V64_PP64_W16>},
     {tiling_of<V64_PP64_QB2_RSS>(), &dispatch_mask<V64_PP64_QB2_RSS>},
     {tiling_of<V128_PP128_RSS>(), &dispatch_mask<V128_PP128_RSS>},
+    {tiling_of<V128_PP128_RSS_M16>(), &dispatch_mask<V128_PP128_RSS_M16>},
 };
 constexpr int kNumEntries = (int)(sizeof(kEntries) / sizeof(kEntries[0]));
 

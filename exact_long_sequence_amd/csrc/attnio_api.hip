@@ -98,10 +98,11 @@ void log_tiling_choice(int d) {
     for (int i = 0; i < n && i < 6; ++i) {
       const attnio::Tiling& t = ev[i].t;
       fprintf(stderr,
-              "[attnio]   BM=%d BN=%d stages=%d waves=%d qb=%d wg/cu=%d %s rowsum=%s vgpr~%d/%d: "
+              "[attnio]   BM=%d BN=%d stages=%d waves=%d qb=%d wg/cu=%d %s rowsum=%s mfma=%s vgpr~%d/%d: "
               "%.4f cyc/pair (issue %.4f, LDS %.1f B, L2->LDS %.2f B, beyond L2 %.4f B)%s\n",
               t.BM, t.BN, t.stages, t.waves, t.qb, t.wg_per_cu, t.pingpong ? "ping-pong" : "sequential",
-              t.rowsum_mfma ? "mfma" : "valu", ev[i].vgpr_estimate, ev[i].vgpr_budget, ev[i].cycles_per_pair,
+              t.rowsum_mfma ? "mfma" : "valu", t.mfma16 ? "16x16x32" : "32x32x16", ev[i].vgpr_estimate,
+              ev[i].vgpr_budget, ev[i].cycles_per_pair,
               ev[i].issue_cycles_per_pair, ev[i].lds_read_bytes_per_pair, ev[i].l2_to_lds_bytes_per_pair,
               ev[i].beyond_l2_bytes_per_pair, ev[i].compiled >= 0 ? " [compiled]" : "");
     }

@@ -63,12 +63,22 @@
 //               2600 cycles per half step, measured 2545);
 //   sequential  n = waves per SIMD, each running both phases: one round =
 //               n M + max(0, n S - rho n M) + 250 for the per-tile barrier.
+//   MFMA shape  the same products on 16x16x32 instead of 32x32x16 (the d = 128
+//               ping-pong form) take the same cycles, but under the chip's
+//               power limit a cycle of the smaller shape costs less: a long
+//               all-CU stream on random operands delivered 0.834 of the bf16
+//               nameplate on 16x16x32 and 0.703 on 32x32x16 (measured).  The
+//               issue price of such a tiling is scaled by 0.703 / 0.834.  (The
+//               kernel gains less than that ratio: it runs 19% faster clocks
+//               but keeps the matrix pipe busy 0.75 instead of 0.86 of them;
+//               measured 3.4% faster at the headline shape.)
 
 #include <math.h>
 #include <string.h>
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "kernels.h"
 
@@ -87,6 +97,7 @@ constexpr double kBarrierCycles = 250.0;  // the sequential form's per-tile barr
 constexpr double kRho = 0.45;             // VALU rate beside a busy MFMA pipe, relative to solo
 constexpr double kDot2Slowdown = 0.59 / 0.37;  // dot2 vs other VALU ops beside an MFMA stream
 constexpr double kPhaseStartCycles = 120.0;
+constexpr double kMfma16PowerRatio = 0.703 / 0.834;  // 32x32x16 vs 16x16x32 delivered rate, power-limited
 
 int read_ahead(int qb) { return qb == 1 ? 4 : 2; }
 
@@ -142,8 +153,10 @@ void price_tiling(TileEval* e) {
     // start its VALU work until that stream ends: no overlap.  (Measured: at
     // 4 reads ahead the softmax wave's placement is 2% faster than the
     // stream's at d = 128; at 2 reads ahead, QB = 2, 1.8% slower at d = 64.)
+    // (In the 16x16x32 form they do not fit, measured: by the softmax wave
+    // 6.38 ms against 6.33 ms in the stream at the headline shape.)
     const bool by_softmax = t.rowsum_mfma && !t.rowsum_in_stream;
-    const bool fits = 16.0 * n_rs <= 32.0 * read_ahead(t.qb);
+    const bool fits = !t.mfma16 && 16.0 * n_rs <= 32.0 * read_ahead(t.qb);
     const double M = 32.0 * (n_pv + n_qk) + (by_softmax ? 0.0 : 16.0 * n_rs) + kPhaseStartCycles;
     // per half step each workgroup's softmax group issues one tile's DMA (K or V)
     const double S = k * vinst * 4.0 + wpc * tile_bytes / kDmaBytesPerClk;
@@ -164,6 +177,7 @@ void price_tiling(TileEval* e) {
     pairs = n * qb * 32.0 * BN;
   }
   e->issue_cycles_per_pair = round / pairs / 4.0;                     // per CU (4 SIMDs)
+  if (t.mfma16) e->issue_cycles_per_pair *= kMfma16PowerRatio;
   e->lds_read_bytes_per_pair = 4.0 * d / (32.0 * qb);
   e->l2_to_lds_bytes_per_pair = 4.0 * d / t.BM;
   e->beyond_l2_bytes_per_pair = 4.0 * d / (32.0 * wpc * t.BM);
@@ -204,7 +218,7 @@ int compiled_index(const Tiling& t) {
     bf16_variant(i, &c);
     if (c.d == t.d && c.BM == t.BM && c.BN == t.BN && c.stages == t.stages && c.waves == t.waves &&
         c.wg_per_cu == t.wg_per_cu && c.qb == t.qb && c.pingpong == t.pingpong &&
-        c.rowsum_mfma == t.rowsum_mfma && c.rowsum_in_stream == t.rowsum_in_stream)
+        c.rowsum_mfma == t.rowsum_mfma && c.rowsum_in_stream == t.rowsum_in_stream && c.mfma16 == t.mfma16)
       return i;
   }
   return -1;
@@ -218,7 +232,7 @@ int enumerate_tilings(int d, TileEval* out, int max_out) {
   static const int kBN[] = {32, 64, 128, 256};
   static const int kStages[] = {2, 3, 4};
   static const int kWPC[] = {1, 2, 3, 4};
-  TileEval all[3 * 2 * 4 * 3 * 4 * 2 * 3];
+  std::vector<TileEval> all(3 * 2 * 4 * 3 * 4 * 2 * 3 * 2);  // every combination (about 440 KB)
   int n = 0;
   for (int w : kWaves)
     for (int qb : kQB)
@@ -226,30 +240,36 @@ int enumerate_tilings(int d, TileEval* out, int max_out) {
         for (int st : kStages)
           for (int wpc : kWPC)
             for (int pp = 0; pp < 2; ++pp)
-              for (int rs = 0; rs < 3; ++rs) {  // VALU; matrix core in the stream; by the softmax wave
-                if (rs == 2 && !pp) continue;
-                TileEval e{};
-                Tiling& t = e.t;
-                t.d = d;
-                t.BM = 32 * w * qb;
-                t.BN = bn;
-                t.stages = st;
-                t.waves = w;
-                t.qb = qb;
-                t.wg_per_cu = wpc;
-                t.pingpong = pp;
-                t.rowsum_mfma = rs > 0;
-                t.rowsum_in_stream = rs == 1;
-                const int ring = st * 2 * bn * d * 2, outb = t.BM * d * 2;
-                t.lds_bytes = std::max(ring, outb) + 16;
-                if (!tiling_fits(t, &e.vgpr_estimate, &e.vgpr_budget)) continue;
-                e.compiled = compiled_index(t);
-                price_tiling(&e);
-                all[n++] = e;
-              }
+              for (int rs = 0; rs < 3; ++rs)  // VALU; matrix core in the stream; by the softmax wave
+                for (int mf = 0; mf < 2; ++mf) {  // MFMA shape: 32x32x16, 16x16x32
+                  if (rs == 2 && !pp) continue;
+                  // the 16x16x32 form is written for d = 128, ping-pong, 32
+                  // queries per wave, row sums on the matrix core
+                  if (mf && !(d == 128 && pp && qb == 1 && rs > 0)) continue;
+                  TileEval e{};
+                  Tiling& t = e.t;
+                  t.d = d;
+                  t.BM = 32 * w * qb;
+                  t.BN = bn;
+                  t.stages = st;
+                  t.waves = w;
+                  t.qb = qb;
+                  t.wg_per_cu = wpc;
+                  t.pingpong = pp;
+                  t.rowsum_mfma = rs > 0;
+                  t.rowsum_in_stream = rs == 1;
+                  t.mfma16 = mf;
+                  const int ring = st * 2 * bn * d * 2, outb = t.BM * d * 2;
+                  t.lds_bytes = std::max(ring, outb) + 16;
+                  if (!tiling_fits(t, &e.vgpr_estimate, &e.vgpr_budget)) continue;
+                  e.compiled = compiled_index(t);
+                  price_tiling(&e);
+                  all[n++] = e;
+                }
   double best = 1e300;
   for (int i = 0; i < n; ++i) best = std::min(best, all[i].cycles_per_pair);
-  std::stable_sort(all, all + n, [best](const TileEval& a, const TileEval& b) { return better(a, b, best); });
+  std::stable_sort(all.begin(), all.begin() + n,
+                   [best](const TileEval& a, const TileEval& b) { return better(a, b, best); });
   for (int i = 0; i < n && i < max_out; ++i) out[i] = all[i];
   return n;
 }

@@ -226,6 +226,8 @@ typedef struct attn_tiling {
   int rowsum_in_stream; /* 1: those row-sum MFMAs issued in the P x V stream of the
                            MFMA phase; 0 (ping-pong only): by the softmax wave at
                            the start of its half step */
+  int mfma16;       /* 1: every product on the 16x16x32 bf16 MFMA (d = 128 ping-pong,
+                       32 queries per wave as two blocks of 16); 0: on 32x32x16 */
 } attn_tiling;
 
 /* Number of bf16 forward tilings compiled into the library, and the shape of

@@ -34,7 +34,8 @@ def _ids():
     out = []
     for i, t in _tilings():
         out.append(f"{i}-d{t['d']}-BM{t['BM']}-BN{t['BN']}-qb{t['qb']}-wpc{t['wg_per_cu']}"
-                   f"-{'pp' if t['pingpong'] else 'seq'}-{'rsv' if not t['rowsum_mfma'] else ('rss' if t['rowsum_in_stream'] else 'rsw')}")
+                   f"-{'pp' if t['pingpong'] else 'seq'}-{'rsv' if not t['rowsum_mfma'] else ('rss' if t['rowsum_in_stream'] else 'rsw')}"
+                   f"{'-m16' if t['mfma16'] else ''}")
     return out
 
 
