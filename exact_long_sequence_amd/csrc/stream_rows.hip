@@ -15,8 +15,11 @@
 // variance), a second pass re-reads the row and writes it.
 //
 // One workgroup of 512 threads per row; a thread owns 8 consecutive elements
-// per 4096-element sweep (16-byte loads and stores).  Rows whose length is not
-// a multiple of 8 take a scalar streaming path.  All arithmetic is fp32; the
+// per 4096-element sweep (16-byte loads and stores).  LayerNorm rows of 512,
+// 1024, 2048, 4096 or 8192 elements go to one wave each instead (eight rows per
+// workgroup): the wave's shuffles reduce the row, with no LDS and no workgroup
+// barrier, and the many rows in flight per CU keep more loads outstanding.  Rows whose length is not a
+// multiple of 8 take a scalar streaming path.  All arithmetic is fp32; the
 // output is rounded to bf16 once.
 
 #include <hip/hip_runtime.h>
@@ -289,6 +292,80 @@ void stream_layernorm_kernel(const __bf16* __restrict__ X, const __bf16* __restr
   }
 }
 
+// LayerNorm, one wave per row, kWaveRows rows per workgroup, for N = 512 * PER
+// (PER = 1, 2, 4, 8, 16) with gamma and beta both given (AFFINE) or both
+// absent: lane l holds elements 512 s + 8 l .. + 7 of sweep s.  Mean, then the
+// mean squared deviation from the registers (the cached kernel's definition),
+// each reduced over the wave by shuffles.  The row is read and written once,
+// so its loads and stores are non-temporal; gamma and beta, shared by every
+// row, go through the caches.  Straight-line code with no per-sweep test lets
+// the compiler keep all of the row's loads, and the next sweeps' gamma and beta
+// loads, in flight.
+constexpr int kWaveRows = 8;
+
+template <int PER, bool AFFINE>
+__global__ __launch_bounds__(64 * kWaveRows)
+void stream_layernorm_wave_kernel(const __bf16* __restrict__ X, const __bf16* __restrict__ gamma,
+                                  const __bf16* __restrict__ beta, __bf16* __restrict__ Y, int R, int N,
+                                  float eps) {
+  const int lane = threadIdx.x % 64;
+  const long long row = (long long)blockIdx.x * kWaveRows + threadIdx.x / 64;
+  if (row >= R) return;  // whole waves only; the kernel has no barrier
+  const __bf16* x = X + row * N;
+  __bf16* y = Y + row * N;
+  bf16x8 xc[PER];
+#pragma unroll
+  for (int s = 0; s < PER; ++s) xc[s] = __builtin_nontemporal_load((const bf16x8*)(x + s * 512 + lane * 8));
+  float s1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < PER; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s1 += (float)xc[s][e];
+#pragma unroll
+  for (int off = 32; off > 0; off /= 2) s1 += __shfl_xor(s1, off);
+  const float inv_n = 1.f / (float)N;
+  const float mu = s1 * inv_n;
+  float s2 = 0.f;
+#pragma unroll
+  for (int s = 0; s < PER; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float dv = (float)xc[s][e] - mu;
+      s2 = __builtin_fmaf(dv, dv, s2);
+    }
+#pragma unroll
+  for (int off = 32; off > 0; off /= 2) s2 += __shfl_xor(s2, off);
+  const float rstd = rsqrtf(s2 * inv_n + eps);
+#pragma unroll
+  for (int s = 0; s < PER; ++s) {
+    const int j = s * 512 + lane * 8;
+    bf16x8 o;
+    if constexpr (AFFINE) {
+      const bf16x8 g = *(const bf16x8*)(gamma + j), b = *(const bf16x8*)(beta + j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)(((float)xc[s][e] - mu) * rstd * (float)g[e] + (float)b[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)(((float)xc[s][e] - mu) * rstd);
+    }
+    __builtin_nontemporal_store(o, (bf16x8*)(y + j));
+  }
+}
+
+template <int PER>
+hipError_t launch_layernorm_wave(const RowArgs& a, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((a.R + kWaveRows - 1) / kWaveRows);
+  if (a.gamma != nullptr)
+    hipLaunchKernelGGL((stream_layernorm_wave_kernel<PER, true>), dim3(blocks), dim3(64 * kWaveRows), 0, stream,
+                       (const __bf16*)a.x, (const __bf16*)a.gamma, (const __bf16*)a.beta, (__bf16*)a.y, a.R,
+                       a.N, a.param);
+  else
+    hipLaunchKernelGGL((stream_layernorm_wave_kernel<PER, false>), dim3(blocks), dim3(64 * kWaveRows), 0, stream,
+                       (const __bf16*)a.x, (const __bf16*)a.gamma, (const __bf16*)a.beta, (__bf16*)a.y, a.R,
+                       a.N, a.param);
+  return hipGetLastError();
+}
+
 // Sweeps held in registers for a row of N elements (0: stream the row).
 int cached_sweeps(int N) {
   if (N % 8 != 0) return 0;
@@ -318,6 +395,17 @@ hipError_t launch_rows(const RowArgs& a, hipStream_t stream) {
 int rows_cached_sweeps(int N) { return cached_sweeps(N); }
 
 hipError_t launch_stream_rows(const RowArgs& a, hipStream_t stream) {
+  // one wave per row: N = 512 * (1, 2, 4, 8 or 16), gamma and beta both given or both absent
+  if (a.op == 1 && a.N % 512 == 0 && a.N <= 8192 && (a.gamma == nullptr) == (a.beta == nullptr)) {
+    switch (a.N / 512) {
+      case 1: return launch_layernorm_wave<1>(a, stream);
+      case 2: return launch_layernorm_wave<2>(a, stream);
+      case 4: return launch_layernorm_wave<4>(a, stream);
+      case 8: return launch_layernorm_wave<8>(a, stream);
+      case 16: return launch_layernorm_wave<16>(a, stream);
+      default: break;
+    }
+  }
   switch (cached_sweeps(a.N)) {
     case 1: return launch_rows<1, true>(a, stream);
     case 2: return launch_rows<2, true>(a, stream);

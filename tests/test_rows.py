@@ -52,8 +52,9 @@ def _check_ln(got, want, gamma, label):
 
 
 # N covers: a single element, ragged (scalar path), one partial sweep, every
-# register-cached sweep count, the largest cached row and streamed rows
-SIZES = [1, 7, 8, 1000, 4096, 4104, 12288, 30000, 65536, 65544, 70001]
+# register-cached sweep count, the largest cached row and streamed rows; for
+# LayerNorm also the one-wave-per-row sizes 512, 2048, 4096 and 8192
+SIZES = [1, 7, 8, 512, 1000, 2048, 4096, 4104, 8192, 12288, 30000, 65536, 65544, 70001]
 
 
 @pytest.mark.parametrize("N", SIZES)
@@ -94,6 +95,23 @@ def test_layernorm_rows(N, affine):
     want = oracle.layernorm_rows_fp64(oracle_view(x), None if gamma is None else oracle_view(gamma),
                                       None if beta is None else oracle_view(beta), eps=1e-5)
     _check_ln(y, want, gamma, f"N={N}")
+
+
+@pytest.mark.parametrize("which", ["gamma", "beta"])
+def test_layernorm_one_affine_vector(which):
+    # only one of gamma and beta given: the workgroup-per-row kernel at a size
+    # that would otherwise take one wave per row
+    R, N = 9, 4096
+    x = _rand((R, N), 3400, sd=2.0, mean=1.0)
+    vec = _rand((N,), 3401, sd=1.0, mean=1.0)
+    gamma, beta = (vec, None) if which == "gamma" else (None, vec)
+    _log(f"layernorm R={R} N={N} only {which}")
+    y = attnio.stream_layernorm(x.to(DEV), None if gamma is None else gamma.to(DEV),
+                                None if beta is None else beta.to(DEV), eps=1e-5)
+    torch.cuda.synchronize()
+    want = oracle.layernorm_rows_fp64(oracle_view(x), None if gamma is None else oracle_view(gamma),
+                                      None if beta is None else oracle_view(beta), eps=1e-5)
+    _check_ln(y, want, gamma, f"only {which}")
 
 
 def test_rows_errors_from_binding():
