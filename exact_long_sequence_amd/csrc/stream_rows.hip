@@ -107,19 +107,29 @@ void stream_softmax_kernel(const __bf16* __restrict__ X, __bf16* __restrict__ Y,
   const __bf16* x = X + (size_t)blockIdx.x * N;
   __bf16* y = Y + (size_t)blockIdx.x * N;
   if (SW > 0) {
-    // cached row: max, then 2^(t - max) kept in registers and summed, then
-    // scaled -- one exponential per element
+    // cached row: max, then the sum of 2^(t - max), then 2^(t - max) again,
+    // scaled and stored.  The row stays packed in registers (an empty asm after
+    // each pass keeps the compiler from holding its fp32 unpacking, and the
+    // exponentials are recomputed rather than kept): 59 instead of 90
+    // registers at 8 sweeps, so more rows are in flight per CU.  The row is
+    // read and written once, so its accesses are non-temporal.  Bitwise the
+    // same result as keeping the exponentials.
     bf16x8 xc[SW > 0 ? SW : 1];
     float xm = -INFINITY;
 #pragma unroll
+    for (int s = 0; s < SW; ++s) {  // past the row's end: the row's first 16 bytes, unused
+      const int j = s * kSweep + tid * 8;
+      xc[s] = __builtin_nontemporal_load((const bf16x8*)(x + (j < N ? j : 0)));
+    }
+#pragma unroll
     for (int s = 0; s < SW; ++s) {
       const int j = s * kSweep + tid * 8;
-      if (j < N) {
-        xc[s] = *(const bf16x8*)(x + j);
+      if (j < N)
 #pragma unroll
         for (int e = 0; e < 8; ++e) xm = fmaxf(xm, (float)xc[s][e]);
-      }
     }
+#pragma unroll
+    for (int s = 0; s < SW; ++s) asm volatile("" : "+v"(xc[s]));
 #pragma unroll
     for (int off = 32; off > 0; off /= 2) xm = fmaxf(xm, __shfl_xor(xm, off));
     if (tid % 64 == 0) red[tid / 64] = xm;
@@ -129,19 +139,16 @@ void stream_softmax_kernel(const __bf16* __restrict__ X, __bf16* __restrict__ Y,
     for (int i = 1; i < 8; ++i) xm = fmaxf(xm, red[i]);
     const bool empty = xm == -INFINITY;
     const float ms = empty ? 0.f : xm * c;  // c > 0: max of x * c is c * max of x
-    float ev[SW > 0 ? SW : 1][8];
     float l = 0.f;
 #pragma unroll
     for (int s = 0; s < SW; ++s) {
       const int j = s * kSweep + tid * 8;
-      if (j < N) {
+      if (j < N)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ev[s][e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)xc[s][e], c, -ms));
-          l += ev[s][e];
-        }
-      }
+        for (int e = 0; e < 8; ++e) l += __builtin_amdgcn_exp2f(__builtin_fmaf((float)xc[s][e], c, -ms));
     }
+#pragma unroll
+    for (int s = 0; s < SW; ++s) asm volatile("" : "+v"(xc[s]));
     float l2 = 0.f;
     block_sum2(l, l2, red);
     const float inv = empty ? 0.f : 1.f / l;
@@ -151,8 +158,9 @@ void stream_softmax_kernel(const __bf16* __restrict__ X, __bf16* __restrict__ Y,
       if (j < N) {
         bf16x8 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (__bf16)(ev[s][e] * inv);
-        *(bf16x8*)(y + j) = o;
+        for (int e = 0; e < 8; ++e)
+          o[e] = (__bf16)(__builtin_amdgcn_exp2f(__builtin_fmaf((float)xc[s][e], c, -ms)) * inv);
+        __builtin_nontemporal_store(o, (bf16x8*)(y + j));
       }
     }
     return;
