@@ -362,7 +362,7 @@ void stream_layernorm_wave_kernel(const __bf16* __restrict__ X, const __bf16* __
 
 template <int PER>
 hipError_t launch_layernorm_wave(const RowArgs& a, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((a.R + kWaveRows - 1) / kWaveRows);
+  const unsigned blocks = (unsigned)(((long long)a.R + kWaveRows - 1) / kWaveRows);  // R up to 2^31 - 1
   if (a.gamma != nullptr)
     hipLaunchKernelGGL((stream_layernorm_wave_kernel<PER, true>), dim3(blocks), dim3(64 * kWaveRows), 0, stream,
                        (const __bf16*)a.x, (const __bf16*)a.gamma, (const __bf16*)a.beta, (__bf16*)a.y, a.R,
