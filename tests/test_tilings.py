@@ -5,7 +5,8 @@ The forward runs the tiling the I/O model picks; the other compiled tilings
 exist to check that choice by measurement, so each must compute the same
 function.  Every row of a small sweep (ragged N, causal, key padding from 0)
 is compared with the oracle at the bf16 tolerance; keys past kv_len are
-NaN-poisoned and must not leak; an input whose probability overflows the
+NaN-poisoned and must not leak; a negative scale (each kernel's other
+instantiation) is checked the same way; an input whose probability overflows the
 first tile's shift without overflowing exp2 (one key 126.96 above it in the
 base-2 domain, |V| = 4) must be recomputed; the picked tiling must be
 bitwise what attn_fwd returns.
@@ -63,6 +64,26 @@ def test_tiling_matches_oracle(index):
                 torch.cuda.synchronize()
                 want = oracle_rows(q, k, v, causal, kv, float(np.float32(1 / np.sqrt(d))), "bf16")
                 compare(gpu_rows(out), want, "bf16", f"tiling {index} N={N} causal={causal} padded={padded}")
+
+
+@pytest.mark.parametrize("index", range(attnio.attn_tiling_count()), ids=_ids())
+def test_tiling_negative_scale(index):
+    """A negative scale takes each kernel's other instantiation (row minimum of
+    the raw scores, masked scores +inf): every row, causal x key padding."""
+    t = attnio.attn_tiling_get(index)
+    d = t["d"]
+    scale = -float(np.float32(0.7 / np.sqrt(d)))
+    for N in (300, 1100):
+        for causal in (False, True):
+            for padded in (False, True):
+                _log(f"tiling {index} d={d} N={N} causal={causal} padded={padded} scale={scale}")
+                q, k, v, kv = make_inputs(2, 3, N, d, "bf16", seed=71 + N, padded=padded, kv_lo=0)
+                kvd = None if kv is None else kv.to(DEV)
+                out = attnio.attn_fwd_tiled(q.to(DEV), k.to(DEV), v.to(DEV), index, causal=causal, kv_len=kvd,
+                                            scale=scale)
+                torch.cuda.synchronize()
+                want = oracle_rows(q, k, v, causal, kv, scale, "bf16")
+                compare(gpu_rows(out), want, "bf16", f"tiling {index} N={N} causal={causal} padded={padded} neg")
 
 
 @pytest.mark.parametrize("index", range(attnio.attn_tiling_count()), ids=_ids())
