@@ -59,13 +59,14 @@ def _check_grad(got, want, label):
     assert mn <= TOL_MEAN * ref_mean + 1e-7, f"{label}: mean_err={mn:.3e} mean|ref|={ref_mean:.3e}"
 
 
-def _run_case(B, H, N, d, causal, padded, seed, q_mul=1.0, kv_lo=0):
+def _run_case(B, H, N, d, causal, padded, seed, q_mul=1.0, kv_lo=0, scale=None):
     q, k, v, kv = make_inputs(B, H, N, d, "bf16", seed, padded=padded, q_mul=q_mul,
                               kv_lo=kv_lo if padded else None)
     do = _dout(q.shape, seed)
-    scale = float(np.float32(1.0 / math.sqrt(d)))
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
     _log(f"bwd case B={B} H={H} N={N} d={d} causal={causal} padded={padded} q_mul={q_mul} "
-         f"seed={seed} kv_len={None if kv is None else kv.tolist()}")
+         f"seed={seed} scale={scale} kv_len={None if kv is None else kv.tolist()}")
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
     kvd = None if kv is None else kv.to(DEV)
     o, lse = attnio.attn_fwd_lse(qd, kd, vd, causal=causal, kv_len=kvd, scale=scale)
@@ -100,6 +101,15 @@ def test_bwd_peaked_softmax(d):
     # Q x 8: near one-hot rows, the regime where P's bf16 rounding matters most
     _run_case(2, 2, 700, d, False, True, seed=950 + d, q_mul=8.0, kv_lo=700 // 4)
     _run_case(1, 2, 513, d, True, False, seed=960 + d, q_mul=8.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_negative_and_zero_scale(d, causal):
+    # P = exp(scale q.k - LSE) for either sign; scale 0 gives uniform P and
+    # dQ = dK = 0 up to the rounding of the zero product
+    _run_case(2, 2, 300, d, causal, True, seed=990 + d + causal, scale=-float(np.float32(0.6 / math.sqrt(d))))
+    _run_case(1, 2, 200, d, causal, False, seed=995 + d + causal, scale=0.0)
 
 
 def test_bwd_empty_keys_and_errors():
