@@ -63,6 +63,23 @@ def test_lse_small_sweep(dtype, d, causal, padded):
         _check_lse(lse.cpu().numpy(), want, dtype, f"N={N}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_lse_negative_scale(dtype, d):
+    # the kernels' negative-scale instantiation (row minimum of the raw scores)
+    fwd_lse = attnio.attn_fwd_lse if dtype == "bf16" else attnio.attn_fwd_f32_lse
+    kind = "bf16" if dtype == "bf16" else "f32"
+    for causal in (False, True):
+        q, k, v, kv = make_inputs(2, 3, 300, d, dtype, 531 + d + causal, padded=True, kv_lo=0)
+        scale = -float(np.float32(0.8 / math.sqrt(d)))
+        _log(f"lse negative scale dtype={dtype} d={d} causal={causal}")
+        o, lse = fwd_lse(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, kv_len=kv.to(DEV), scale=scale)
+        torch.cuda.synchronize()
+        want = oracle.attention_lse_fp64(oracle_view(q), oracle_view(k), oracle_view(v), scale, causal,
+                                         kv.numpy(), kind=kind)
+        _check_lse(lse.cpu().numpy(), want, dtype, f"negative scale causal={causal}")
+
+
 def test_lse_headline_workload_sampled():
     w = WORKLOADS["bf16_causal_h32_n32k_d128"]
     _log("lse headline: inputs")
