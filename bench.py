@@ -94,8 +94,9 @@ PAGE_CONTEXT = {
 def committed_counters(w, ms: float):
     """Issue and utilization figures of workload w from the committed
     rocprofv3 summaries, when they were taken on the current kernel source:
-    MFMA pipe busy, other VALU instructions per MFMA, LDS bank-conflict cycles
-    per LDS-active cycle, the clock the kernel ran at, and the HBM bytes of
+    MFMA pipe busy, other VALU instructions per MFMA, the VALU-active fraction
+    (which counts MFMA issue too), LDS bank-conflict cycles per LDS-active
+    cycle, the clock the kernel ran at, and the HBM bytes of
     the counter summary divided by this run's time."""
     stem = counter_summary_path(w)[:-len("_counters.md")]
     out = {}
@@ -109,6 +110,7 @@ def committed_counters(w, ms: float):
                 return float(m.group(1)) if m else None
             out["mfma_pipe_busy"] = num(r"MFMA pipe busy: .* = ([0-9.]+)")
             out["valu_per_mfma"] = num(r"other VALU instructions per MFMA: .* = ([0-9.]+)")
+            out["valu_active"] = num(r"VALU active \(.*\): .* = ([0-9.]+)")
             conf = re.search(r"LDS bank conflict cycles / LDS active cycles: ([0-9.e+]+) / ([0-9.e+]+)", text)
             out["lds_bank_conflict_rate"] = float(conf.group(1)) / float(conf.group(2)) if conf else None
             out["clock_ghz"] = num(r"clock during the kernel: .* = ([0-9.]+) GHz")
