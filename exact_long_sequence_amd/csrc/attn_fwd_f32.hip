@@ -8,8 +8,10 @@
 // latency rather than throughput, so it trades MFMA for parallelism over keys:
 //
 //   workgroup = 256 threads = 8 queries x 32 key lanes
-//   each thread runs its own online softmax over keys j = 16*t + lane of every
-//   64-key LDS tile, with its own (m, l, acc[d]) state;
+//   each thread runs its own online softmax over keys j = 32*t + lane of every
+//   64-key LDS tile, with its own (m, l, acc[d]) state, rescaled once per
+//   tile and only when some lane's running extreme moved;
+//   K/V tiles are prefetched into registers one tile ahead of the LDS copy;
 //   the 32 partial states of a query are merged at the end with the same
 //   rescale the online update uses (the streaming reduction merges exactly:
 //   "IO-Aware Algorithms", How it works, online softmax).
@@ -25,15 +27,18 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// 8 x 32: measured on MI355X at N = 1024, d = 64, 44 us per call against
-// 64 us for 16 x 16 (64 workgroups on 256 CUs) and 77 us for 4 x 64 (merge
-// cost); a 1024-row head is latency-bound, so the split favours parallelism
+// 8 x 32: measured on MI355X at N = 1024, d = 64 (before the K/V prefetch
+// below), 44 us per call against 64 us for 16 x 16 (64 workgroups on 256 CUs)
+// and 77 us for 4 x 64; 8 x 64 (two waves per SIMD) ran 91 us: a merge across
+// 64 lanes exchanges between the two halves of the wave.  A 1024-row head is
+// latency-bound, so the split favours parallelism
 constexpr int kQ = 8;         // queries per workgroup
 constexpr int kLanes = 32;    // key lanes per query
 constexpr int kBN = 64;       // keys per LDS tile
+constexpr int THREADS = kQ * kLanes;
 
 template <int D, bool CAUSAL, bool NEG>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(THREADS)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, float* __restrict__ O,
                          const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
@@ -66,7 +71,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   const float* Vs = V + slice;
   float* Os = O + slice;
 
-  for (int e = tid; e < kQ * D / 4; e += 256) {
+  for (int e = tid; e < kQ * D / 4; e += THREADS) {
     const int r = e / (D / 4), c4 = e % (D / 4);
     const int gr = min(q0 + r, N - 1);
     *(float4*)&qs[r * P + c4 * 4] = *(const float4*)&Qs[(size_t)gr * D + c4 * 4];
@@ -79,46 +84,90 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 #pragma unroll
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
 
-  for (int j0 = 0; j0 < kend; j0 += kBN) {
-    __syncthreads();
-    for (int e = tid; e < kBN * D / 4; e += 256) {
+  // K/V tiles go HBM -> registers -> LDS: the loads of tile j0 + kBN are in
+  // flight while tile j0 is computed, and stored to LDS after the barrier
+  constexpr int NL = kBN * D / 4 / THREADS;  // 16-byte loads of K (and of V) per thread
+  static_assert(kBN * D / 4 % THREADS == 0, "a tile must split evenly over the threads");
+  typedef float f32x4 __attribute__((ext_vector_type(4)));  // a native vector: kept in registers
+  f32x4 kreg[NL], vreg[NL];
+  if (kend > 0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * THREADS;
       const int r = e / (D / 4), c4 = e % (D / 4);
-      const int gr = min(j0 + r, kend - 1);
-      *(float4*)&ks[r * P + c4 * 4] = *(const float4*)&Ks[(size_t)gr * D + c4 * 4];
-      *(float4*)&vs[r * P + c4 * 4] = *(const float4*)&Vs[(size_t)gr * D + c4 * 4];
+      const int gr = min(r, kend - 1);
+      kreg[i] = *(const f32x4*)&Ks[(size_t)gr * D + c4 * 4];
+      vreg[i] = *(const f32x4*)&Vs[(size_t)gr * D + c4 * 4];
+    }
+  }
+  for (int j0 = 0; j0 < kend; j0 += kBN) {
+    __syncthreads();  // every read of the previous tile is done
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * THREADS;
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      *(f32x4*)&ks[r * P + c4 * 4] = kreg[i];
+      *(f32x4*)&vs[r * P + c4 * 4] = vreg[i];
     }
     __syncthreads();
-#pragma unroll 1
-    for (int t = 0; t < kBN / kLanes; ++t) {
+    // the next tile (past the last one: rows clamped to kend - 1, unused)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int e = tid + i * THREADS;
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      const int gr = min(j0 + kBN + r, kend - 1);
+      kreg[i] = *(const f32x4*)&Ks[(size_t)gr * D + c4 * 4];
+      vreg[i] = *(const f32x4*)&Vs[(size_t)gr * D + c4 * 4];
+    }
+    // the lane's keys of this tile: scores first, then one update of the
+    // running extreme for all of them, a rescale of the state only when some
+    // lane's extreme moved (a wave-uniform test), and one fma per key and
+    // element for the accumulation
+    constexpr int KPL = kBN / kLanes;  // keys per lane per tile
+    float sc[KPL];
+    bool okk[KPL];
+    float m_new = m;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) {
       const int jl = t * kLanes + kl;
       const int key = j0 + jl;
       bool ok = key < kend;
       if (CAUSAL) ok = ok && key <= qrow;
-      float s = 0.f;
+      float sv = 0.f;
 #pragma unroll
       for (int e = 0; e < D; e += 4) {
         const float4 a = *(const float4*)&qs[qi * P + e];
         const float4 k4 = *(const float4*)&ks[jl * P + e];
-        s = __builtin_fmaf(a.x, k4.x, s);
-        s = __builtin_fmaf(a.y, k4.y, s);
-        s = __builtin_fmaf(a.z, k4.z, s);
-        s = __builtin_fmaf(a.w, k4.w, s);
+        sv = __builtin_fmaf(a.x, k4.x, sv);
+        sv = __builtin_fmaf(a.y, k4.y, sv);
+        sv = __builtin_fmaf(a.z, k4.z, sv);
+        sv = __builtin_fmaf(a.w, k4.w, sv);
       }
-      if (!ok) continue;
-      // online update with the raw-score extreme m; weights exp2((s - m) * c)
-      const float m_new = NEG ? fminf(m, s) : fmaxf(m, s);
+      sc[t] = sv;
+      okk[t] = ok;
+      if (ok) m_new = NEG ? fminf(m_new, sv) : fmaxf(m_new, sv);
+    }
+    if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
+      // weights exp2((s - m) * c) are relative to the raw-score extreme m
       const float alpha = (m == m_new) ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * c);
-      const float p = __builtin_amdgcn_exp2f((s - m_new) * c);
-      l = l * alpha + p;
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] *= alpha;
+      m = m_new;
+    }
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) {
+      const int jl = t * kLanes + kl;
+      const float p = okk[t] ? __builtin_amdgcn_exp2f((sc[t] - m) * c) : 0.f;
+      l += p;
 #pragma unroll
       for (int e = 0; e < D; e += 4) {
         const float4 v4 = *(const float4*)&vs[jl * P + e];
-        acc[e + 0] = __builtin_fmaf(p, v4.x, acc[e + 0] * alpha);
-        acc[e + 1] = __builtin_fmaf(p, v4.y, acc[e + 1] * alpha);
-        acc[e + 2] = __builtin_fmaf(p, v4.z, acc[e + 2] * alpha);
-        acc[e + 3] = __builtin_fmaf(p, v4.w, acc[e + 3] * alpha);
+        acc[e + 0] = __builtin_fmaf(p, v4.x, acc[e + 0]);
+        acc[e + 1] = __builtin_fmaf(p, v4.y, acc[e + 1]);
+        acc[e + 2] = __builtin_fmaf(p, v4.z, acc[e + 2]);
+        acc[e + 3] = __builtin_fmaf(p, v4.w, acc[e + 3]);
       }
-      m = m_new;
     }
   }
 
@@ -164,7 +213,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   // normal float so that (-inf) * c stays -inf (uniform weights, no NaN)
   float c = a.scale * kLog2e;
   if (c == 0.f) c = FLT_MIN;
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(256), 0,
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(THREADS), 0,
                      stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
                      a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
