@@ -7,13 +7,15 @@
 // intermediate.  This path serves small fp32 problems, which are bound by
 // latency rather than throughput, so it trades MFMA for parallelism over keys:
 //
-//   workgroup = 256 threads = 8 queries x 32 key lanes
+//   workgroup = 8 queries x 32 key lanes (256 threads), two such groups at
+//   d = 64 taking the even and the odd key tiles (512 threads)
 //   each thread runs its own online softmax over keys j = 32*t + lane of every
 //   64-key LDS tile, with its own (m, l, acc[d]) state, rescaled once per
 //   tile and only when some lane's running extreme moved;
 //   K/V tiles are prefetched into registers one tile ahead of the LDS copy;
-//   the 32 partial states of a query are merged at the end with the same
-//   rescale the online update uses (the streaming reduction merges exactly:
+//   the 32 partial states of a query (and at d = 64 those of the two groups,
+//   through LDS) are merged at the end with the same rescale the online update
+//   uses (the streaming reduction merges exactly:
 //   "IO-Aware Algorithms", How it works, online softmax).
 
 #include <hip/hip_runtime.h>
@@ -35,22 +37,33 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQ = 8;         // queries per workgroup
 constexpr int kLanes = 32;    // key lanes per query
 constexpr int kBN = 64;       // keys per LDS tile
-constexpr int THREADS = kQ * kLanes;
+constexpr int kHalf = kQ * kLanes;  // threads that walk one key sequence
+// key halves per workgroup: at d = 64 two groups of 256 threads take the even
+// and the odd key tiles of the same queries (8 waves, two per SIMD, half the
+// keys per thread) and merge their states through LDS at the end; at d = 128
+// the fp32 accumulators of two waves per SIMD do not fit the registers
+template <int D>
+constexpr int halves_of() { return D == 64 ? 2 : 1; }
 
 template <int D, bool CAUSAL, bool NEG>
-__global__ __launch_bounds__(THREADS)
+__global__ __launch_bounds__(kHalf * halves_of<D>())
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, float* __restrict__ O,
                          const int32_t* __restrict__ kv_len, float* __restrict__ lse, int H,
                          int N, float c, int n_qtiles) {
+  constexpr int HALVES = halves_of<D>();
+  constexpr int THREADS = kHalf * HALVES;
   constexpr int P = D + 4;  // padded LDS row (floats): keeps 16 rows on distinct banks
   __shared__ __attribute__((aligned(16))) float qs[kQ * P];
-  __shared__ __attribute__((aligned(16))) float ks[kBN * P];
-  __shared__ __attribute__((aligned(16))) float vs[kBN * P];
+  __shared__ __attribute__((aligned(16))) float kvs[HALVES][2][kBN * P];  // per half: K tile, V tile
 
   const int tid = threadIdx.x;
-  const int qi = tid / kLanes;
-  const int kl = tid % kLanes;
+  const int hf = tid / kHalf;  // key half: tiles hf, hf + HALVES, ...
+  const int ht = tid % kHalf;
+  const int qi = ht / kLanes;
+  const int kl = ht % kLanes;
+  float* ks = kvs[hf][0];
+  float* vs = kvs[hf][1];
 
   const int bh = blockIdx.x / n_qtiles;
   int qt = blockIdx.x % n_qtiles;
@@ -84,38 +97,44 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 #pragma unroll
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
 
-  // K/V tiles go HBM -> registers -> LDS: the loads of tile j0 + kBN are in
-  // flight while tile j0 is computed, and stored to LDS after the barrier
-  constexpr int NL = kBN * D / 4 / THREADS;  // 16-byte loads of K (and of V) per thread
-  static_assert(kBN * D / 4 % THREADS == 0, "a tile must split evenly over the threads");
+  // K/V tiles go HBM -> registers -> LDS: the loads of a half's next tile are
+  // in flight while its current one is computed, and stored to LDS after the
+  // barrier.  Half hf takes tiles hf, hf + HALVES, ...; both halves run the
+  // same number of steps (a step past the last tile has no valid key, and its
+  // loads are clamped to row kend - 1), so every thread meets every barrier.
+  constexpr int NL = kBN * D / 4 / kHalf;  // 16-byte loads of K (and of V) per thread
+  static_assert(kBN * D / 4 % kHalf == 0, "a tile must split evenly over a half's threads");
   typedef float f32x4 __attribute__((ext_vector_type(4)));  // a native vector: kept in registers
   f32x4 kreg[NL], vreg[NL];
+  const int n_tiles = (kend + kBN - 1) / kBN;
+  const int n_steps = (n_tiles + HALVES - 1) / HALVES;
   if (kend > 0) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int e = tid + i * THREADS;
+      const int e = ht + i * kHalf;
       const int r = e / (D / 4), c4 = e % (D / 4);
-      const int gr = min(r, kend - 1);
+      const int gr = min(hf * kBN + r, kend - 1);
       kreg[i] = *(const f32x4*)&Ks[(size_t)gr * D + c4 * 4];
       vreg[i] = *(const f32x4*)&Vs[(size_t)gr * D + c4 * 4];
     }
   }
-  for (int j0 = 0; j0 < kend; j0 += kBN) {
-    __syncthreads();  // every read of the previous tile is done
+  for (int step = 0; step < n_steps; ++step) {
+    const int j0 = (step * HALVES + hf) * kBN;
+    __syncthreads();  // every read of the previous tiles is done
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int e = tid + i * THREADS;
+      const int e = ht + i * kHalf;
       const int r = e / (D / 4), c4 = e % (D / 4);
       *(f32x4*)&ks[r * P + c4 * 4] = kreg[i];
       *(f32x4*)&vs[r * P + c4 * 4] = vreg[i];
     }
     __syncthreads();
-    // the next tile (past the last one: rows clamped to kend - 1, unused)
+    // the half's next tile (past the last one: rows clamped to kend - 1, unused)
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int e = tid + i * THREADS;
+      const int e = ht + i * kHalf;
       const int r = e / (D / 4), c4 = e % (D / 4);
-      const int gr = min(j0 + kBN + r, kend - 1);
+      const int gr = min(j0 + HALVES * kBN + r, kend - 1);
       kreg[i] = *(const f32x4*)&Ks[(size_t)gr * D + c4 * 4];
       vreg[i] = *(const f32x4*)&Vs[(size_t)gr * D + c4 * 4];
     }
@@ -184,7 +203,6 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   l *= w;
 #pragma unroll
   for (int off = kLanes / 2; off > 0; off /= 2) l += __shfl_xor(l, off, kLanes);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     float x = acc[e] * w;
@@ -192,12 +210,43 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     for (int off = kLanes / 2; off > 0; off /= 2) x += __shfl_xor(x, off, kLanes);
     acc[e] = x;
   }
+  constexpr int PER = D / kLanes;  // output elements of each lane: kl * PER ..
+  if constexpr (HALVES == 2) {
+    // half 1 hands its merged (m, l, acc) of each query to half 0 through LDS
+    // (the K/V tiles are dead); half 0 merges them with the same rescale
+    constexpr int XS = D + 2;  // per query: m, l, acc[D]
+    static_assert(kQ * XS <= HALVES * 2 * kBN * P, "exchange fits the tile area");
+    float* xch = &kvs[0][0][0];
+    __syncthreads();
+    if (hf == 1) {
+      if (kl == 0) {
+        xch[qi * XS] = m_all;
+        xch[qi * XS + 1] = l;
+      }
+#pragma unroll
+      for (int e = 0; e < D; ++e)
+        if (e / PER == kl) xch[qi * XS + 2 + e] = acc[e];
+    }
+    __syncthreads();
+    if (hf == 1) return;  // no barrier follows
+    const float m1 = xch[qi * XS], l1 = xch[qi * XS + 1];
+    const float mm = NEG ? fminf(m_all, m1) : fmaxf(m_all, m1);
+    const bool e0 = NEG ? (m_all == INFINITY) : (m_all == -INFINITY);
+    const bool e1 = NEG ? (m1 == INFINITY) : (m1 == -INFINITY);
+    const float w0 = e0 ? 0.f : __builtin_amdgcn_exp2f((m_all - mm) * c);
+    const float w1 = e1 ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * c);
+    l = l * w0 + l1 * w1;
+#pragma unroll
+    for (int e = 0; e < D; ++e)
+      if (e / PER == kl) acc[e] = acc[e] * w0 + xch[qi * XS + 2 + e] * w1;
+    m_all = mm;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   // log-sum-exp: sum_j 2^(c s_j) = 2^(c m_all) * l (m_all is the raw-score
   // extreme, c * m_all the largest exponent whatever the sign of c)
   if (lse != nullptr && kl == 0 && qrow < N)
     lse[(size_t)bh * N + qrow] = l > 0.f ? (m_all * c + log2f(l)) * kLn2 : -INFINITY;
   if (qrow < N) {
-    constexpr int PER = D / kLanes;
 #pragma unroll
     for (int e = 0; e < D; ++e)
       if (e / PER == kl) Os[(size_t)qrow * D + e] = acc[e] * inv;
@@ -213,7 +262,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   // normal float so that (-inf) * c stays -inf (uniform weights, no NaN)
   float c = a.scale * kLog2e;
   if (c == 0.f) c = FLT_MIN;
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(THREADS), 0,
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, NEG>), dim3((unsigned)grid), dim3(kHalf * halves_of<D>()), 0,
                      stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o,
                      a.kv_len, a.lse, a.H, a.N, c, n_qtiles);
   return hipGetLastError();
